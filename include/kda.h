@@ -1,0 +1,166 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library
+ *          (libkda.so).
+ *
+ * The operator (per head; q_t, k_t in R^{d_k}, v_t in R^{d_v}, beta_t in (0,1)):
+ *
+ *   gate     g_t = g_min * Sigmoid(exp(A_h) * z_t),  alpha_t = exp(g_t)
+ *            ("Kimi K3 模型结构（2）：序列维度（下）", section "K3 的改动：下界衰减",
+ *            equation (5); z_t are the gate logits, one per key channel)
+ *   update   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *            ("Kimi K3 模型结构（7）：结构决定系统", section "KDA 上下文并行", eq. (1))
+ *   output   o_t = S_t^T q_t  (read after the update)
+ *
+ * S is d_k x d_v (row i = key channel i) and is always fp32.  Only
+ * d_k = d_v = 128 is supported.
+ *
+ * Conventions shared by every entry point
+ *   * Tensor pointers are DEVICE pointers to contiguous row-major arrays unless
+ *     a name ends in _host.  Token-major layouts: x[t][h][c].
+ *   * dtype selects the element type of q, k, v, g_logits, beta and o
+ *     (KDA_F32 or KDA_BF16).  States are fp32 in every mode.
+ *   * q and k are taken as given (callers L2-normalise them); beta is taken as
+ *     given, already in (0,1).  The gate is applied inside the kernels.
+ *   * The caller owns every buffer, including workspaces.  The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream).  Return codes describe
+ *     argument validation and launch status only; kernels run asynchronously.
+ *   * Every argument the host can check is checked before any HIP call;
+ *     failures return a negative kda_status and enqueue nothing.
+ *   * Values the host cannot see (device-resident lengths) are clamped in the
+ *     kernel and reported through an optional device error flag.
+ *   * No C++ exception crosses this interface.  kda_last_error() returns a
+ *     thread-local description of the last non-OK return.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,       /* a size is out of range (d_k, d_v != 128, H <= 0, ...) */
+  KDA_ERR_DTYPE = -3,       /* unknown dtype or compute mode */
+  KDA_ERR_GATE_BOUND = -4,  /* g_min outside [-5, 0): the 16-token subtile factors
+                               could leave the bf16 range ("5 x 16 = 80") */
+  KDA_ERR_SEQLENS = -5,     /* cu_seqlens not 0-based, not monotone, or not ending at T */
+  KDA_ERR_WORKSPACE = -6,   /* workspace NULL, misaligned or smaller than required */
+  KDA_ERR_HIP = -7,         /* a HIP launch failed (see kda_last_error) */
+  KDA_ERR_UNSUPPORTED = -8  /* valid request this build does not implement */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Arithmetic of the prefill paths.  KDA_COMPUTE_AUTO picks bf16 MFMA operands
+ * with fp32 accumulation for bf16 inputs and fp32 MFMA for fp32 inputs;
+ * KDA_COMPUTE_F32 forces the fp32 verification arithmetic for either dtype. */
+typedef enum kda_compute { KDA_COMPUTE_AUTO = 0, KDA_COMPUTE_F32 = 1 } kda_compute;
+
+/* ------------------------------------------------------------------------- */
+/* kda_chunk_fwd -- chunkwise prefill of packed documents.
+ *
+ * Computes the operator over each document of a packed token sequence using the
+ * chunkwise form with chunk C = 64 and 16-token subtiles: the UT transform
+ * (I + StrictTril(Diag(beta) K_decay K_inv^T))^-1 ("序列维度（下）", section
+ * "UT 变换") and the chunk recurrence
+ *     U = INV Diag(beta) (V - K_decay S),  O = Q_decay S + M_qk U,
+ *     S <- Diag(gamma^C) S + K_restore^T U
+ * (SemiAnalysis page "Kimi K3 ...", section "FlashKDA 算法").  Chunks restart at
+ * every document start; the state is reset there (systems page, "文档边界").
+ *
+ *   q, k, g_logits  [T, H, 128]  dtype
+ *   v               [T, H, 128]  dtype
+ *   beta            [T, H]       dtype, values in (0,1)
+ *   A_log           [H] fp32 per-head log scale A_h, or NULL (A_h = 0)
+ *   g_min           lower bound of the log-decay; must satisfy -5 <= g_min < 0
+ *   initial_state   [N, H, 128, 128] fp32 or NULL (zero states)
+ *   cu_seqlens      [N+1] int32 device copy of the document offsets, or NULL
+ *                   for a single document of T tokens (then N must be 1)
+ *   cu_seqlens_host the same offsets in host memory (validated here: cu[0] = 0,
+ *                   non-decreasing, cu[N] = T); required when cu_seqlens != NULL
+ *   o               [T, H, 128]  dtype (written)
+ *   final_state     [N, H, 128, 128] fp32 or NULL; may alias initial_state
+ *   compute         kda_compute
+ * No workspace is needed: each workgroup keeps its state slice in registers.
+ * T = 0 is valid (nothing is written except final_state = initial_state). */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_logits,
+                  const void *beta, const float *A_log, float g_min,
+                  const float *initial_state, const int32_t *cu_seqlens,
+                  const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                  int32_t dk, int32_t dv, int32_t dtype, int32_t compute, void *o,
+                  float *final_state, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* kda_segment_scan -- intra-device context parallelism for long prefill.
+ *
+ * Same operator and arguments as kda_chunk_fwd.  The packed sequence is cut into
+ * n_segments equal token ranges (the last one ragged).  Following equation (17)
+ * of the systems page and its derivation (section "公式 (17) 的推导"):
+ *   A. each (segment, head) computes its affine pair (M, S~) from a zero state
+ *      (M = product of the per-token transitions; M = 0 when a document starts
+ *      inside the segment, whose S~ then starts from that document's state);
+ *   B. per head, entry states are scanned: E_0 = S0, E_{j+1} = M_j E_j + S~_j,
+ *      reset to the document's initial state where a document starts exactly on
+ *      a segment boundary;
+ *   C. every segment is re-run from its exact entry state, producing O and the
+ *      final state of every document.
+ * n_segments <= 0 means one segment per compute unit of the current device.
+ * workspace: device memory of at least kda_segment_scan_workspace_size() bytes,
+ * 256-byte aligned; its contents on entry are ignored. */
+size_t kda_segment_scan_workspace_size(int32_t n_segments, int32_t H, int32_t dk, int32_t dv);
+
+int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_logits,
+                     const void *beta, const float *A_log, float g_min,
+                     const float *initial_state, const int32_t *cu_seqlens,
+                     const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                     int32_t dk, int32_t dv, int32_t dtype, int32_t compute,
+                     int32_t n_segments, void *o, float *final_state, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Number of segments kda_segment_scan uses for n_segments <= 0 (the compute-unit
+ * count of the current device), or a negative kda_status. */
+int kda_default_segments(void);
+
+/* ------------------------------------------------------------------------- */
+/* kda_decode_step -- one decode step with speculative-verify replay.
+ *
+ * For every sequence n and head h, starting from the saved state
+ * state[slot(n), h]: replay the first accepted[n] cached draft tokens, then the
+ * bonus token, one recurrence step each in fp32 (delta form of the SemiAnalysis
+ * page, section "FlashKDA 算法"; replay design of the systems page, section
+ * "KDA：三种执行形态" on decode).  The state after the bonus token is written
+ * back in place and o receives the bonus token's output.
+ *
+ *   state        [S_pool, H, 128, 128] fp32, read and written in place
+ *   state_slots  [N] int32 slot of each sequence in the pool, or NULL (slot = n)
+ *   cq, ck, cv, cz  [N, W, H, 128] dtype  cached projected draft inputs
+ *   cbeta        [N, W, H] dtype
+ *   accepted     [N] int32 device; values outside [0, W] are clamped and
+ *                reported through err_flag
+ *   nq, nk, nv, nz  [N, H, 128] dtype  bonus-token inputs;  nbeta [N, H]
+ *   A_log        [H] fp32 or NULL;  g_min as for kda_chunk_fwd
+ *   o            [N, H, 128] dtype (written)
+ *   err_flag     int32 device pointer or NULL; set to 1 when a length was clamped
+ *                (never cleared by the library)
+ * Slots must be distinct across the N sequences of one call. */
+int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
+                    const void *cv, const void *cz, const void *cbeta,
+                    const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                    const void *nv, const void *nz, const void *nbeta, const float *A_log,
+                    float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
+                    int32_t dv, int32_t dtype, void *stream);
+
+/* ------------------------------------------------------------------------- */
+const char *kda_status_string(int status);  /* static string */
+const char *kda_last_error(void);           /* thread-local detail of the last failure */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

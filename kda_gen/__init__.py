@@ -281,3 +281,26 @@ def workload(idx: int, *, scale_T: Optional[int] = None, scale_H: Optional[int] 
     if idx == 4:
         return make_decode(4, scale_N or 512, scale_H or 96, 4, "bf16")
     raise ValueError(idx)
+
+
+# ----------------------------------------------------------------------------
+# Moving inputs to a device (storage only)
+# ----------------------------------------------------------------------------
+def to_torch(t, device="cuda"):
+    """kda_gen.Tensor (or float32 ndarray) -> torch tensor on ``device``.
+    bf16 bit patterns become torch.bfloat16 without any rounding."""
+    import torch
+    if isinstance(t, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(t)).to(device)
+    if t.dtype == "bf16":
+        return torch.from_numpy(t.data.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(t.data).to(device)
+
+
+def from_torch(x) -> np.ndarray:
+    """torch tensor (bf16 or fp32) -> float64 numpy array with the exact values."""
+    import torch
+    x = x.detach().to("cpu")
+    if x.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(x.view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
+    return x.to(torch.float64).numpy()

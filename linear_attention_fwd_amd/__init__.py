@@ -1,0 +1,245 @@
+"""Python binding of libkda.so, the MI355X (gfx950) Kimi Delta Attention forward.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+behind the C ABI declared in ``include/kda.h``.  PyTorch provides device memory
+and the current stream.  There is no fallback: if the library is missing or the
+tensors are not on a GPU, calls raise.
+
+Entry points (same names as the C ABI):
+  * ``kda_chunk_fwd``    -- chunkwise prefill of packed documents
+  * ``kda_segment_scan`` -- prefill with intra-device segment pairs + scan
+  * ``kda_decode_step``  -- decode step with speculative-verify replay
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
+STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
+          -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
+          -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
+EXPORTS = ("kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
+           "kda_default_segments", "kda_decode_step", "kda_status_string", "kda_last_error")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        super().__init__(f"{STATUS.get(code, code)}: {detail}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with linear_attention_fwd_amd._build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_segment_scan.argtypes = prefill + [i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_segment_scan.restype = ctypes.c_int
+    lib.kda_segment_scan_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kda_segment_scan_workspace_size.restype = ctypes.c_size_t
+    lib.kda_default_segments.argtypes = []
+    lib.kda_default_segments.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                    f32, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise KDAError(rc, _lib.kda_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _seqlens(cu_seqlens, cu_seqlens_host, T, device):
+    """Return (device int32 tensor or None, host int32 numpy array or None, N)."""
+    torch = _torch()
+    if cu_seqlens is None and cu_seqlens_host is None:
+        return None, None, 1
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.detach().to("cpu")
+    host = np.ascontiguousarray(np.asarray(cu_seqlens_host.numpy() if hasattr(cu_seqlens_host, "numpy")
+                                           else cu_seqlens_host), dtype=np.int32)
+    if cu_seqlens is None or not getattr(cu_seqlens, "is_cuda", False):
+        cu_seqlens = torch.from_numpy(host).to(device)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    return cu_seqlens, host, int(host.shape[0] - 1)
+
+
+def _prefill_common(q, k, v, g_logits, beta, A_log, initial_state, cu_seqlens, cu_seqlens_host):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_logits", g_logits), ("beta", beta)):
+        _dev(t, name, q.dtype)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != (T, H, dk) or g_logits.shape != (T, H, dk) or v.shape[:2] != (T, H) \
+            or beta.shape != (T, H):
+        raise ValueError("shape mismatch: q,k,g_logits [T,H,dk], v [T,H,dv], beta [T,H]")
+    _dev(A_log, "A_log", torch.float32)
+    cu_dev, cu_host, N = _seqlens(cu_seqlens, cu_seqlens_host, T, q.device)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32)
+        if tuple(initial_state.shape) != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be [{N},{H},{dk},{dv}]")
+    return T, H, dk, dv, N, cu_dev, cu_host
+
+
+def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
+                  initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                  output_final_state: bool = True, compute: int = KDA_COMPUTE_AUTO,
+                  o=None, final_state=None) -> Tuple[object, Optional[object]]:
+    """Chunkwise KDA prefill.  q, k, v, g_logits: [T, H, 128]; beta: [T, H] (same
+    dtype, bf16 or fp32); A_log: [H] fp32 or None; initial_state: [N, H, 128, 128]
+    fp32 or None; cu_seqlens: [N+1] int32 (device and/or host copy).
+    Returns (o [T, H, 128] in the input dtype, final_state [N, H, 128, 128] fp32 or None)."""
+    torch = _torch()
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
+                                                       initial_state, cu_seqlens, cu_seqlens_host)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
+                           float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
+                           dk, dv, _dtype_code(q), int(compute), _ptr(o), _ptr(final_state),
+                           _stream())
+    _check(rc)
+    return o, final_state
+
+
+def kda_segment_scan_workspace_size(n_segments: int, H: int, dk: int = 128, dv: int = 128) -> int:
+    return int(load_library().kda_segment_scan_workspace_size(n_segments, H, dk, dv))
+
+
+def kda_default_segments() -> int:
+    n = int(load_library().kda_default_segments())
+    if n < 0:
+        _check(n)
+    return n
+
+
+def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
+                     initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                     n_segments: int = 0, output_final_state: bool = True,
+                     compute: int = KDA_COMPUTE_AUTO, workspace=None, o=None,
+                     final_state=None):
+    """Prefill via per-segment affine pairs, an on-device pair scan and a re-run
+    from exact entry states.  Same tensors as ``kda_chunk_fwd``; n_segments <= 0
+    uses one segment per compute unit.  Returns (o, final_state)."""
+    torch = _torch()
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
+                                                       initial_state, cu_seqlens, cu_seqlens_host)
+    n_seg = n_segments if n_segments > 0 else kda_default_segments()
+    n_seg = max(1, min(n_seg, max(T, 1)))
+    seg_len = -(-max(T, 1) // n_seg)
+    n_seg = -(-max(T, 1) // seg_len)
+    need = kda_segment_scan_workspace_size(n_seg, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.kda_segment_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
+                              float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
+                              dk, dv, _dtype_code(q), int(compute), int(n_seg), _ptr(o),
+                              _ptr(final_state), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream())
+    _check(rc)
+    return o, final_state
+
+
+def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
+                    A_log=None, g_min: float = -5.0, state_slots=None, o=None, err_flag=None):
+    """One decode step with speculative-verify replay, updating ``state`` in place.
+
+    state: [S_pool, H, 128, 128] fp32; cq, ck, cv, cz: [N, W, H, 128]; cbeta: [N, W, H];
+    accepted: [N] int32 (device); nq, nk, nv, nz: [N, H, 128]; nbeta: [N, H].
+    Returns o [N, H, 128] (output of the bonus token)."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    N, H, d = nq.shape
+    W = cq.shape[1] if cq is not None else 0
+    dt = nq.dtype
+    for name, t in (("cq", cq), ("ck", ck), ("cv", cv), ("cz", cz), ("cbeta", cbeta), ("nq", nq),
+                    ("nk", nk), ("nv", nv), ("nz", nz), ("nbeta", nbeta)):
+        _dev(t, name, dt)
+    _dev(accepted, "accepted", torch.int32)
+    _dev(state_slots, "state_slots", torch.int32)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(err_flag, "err_flag", torch.int32)
+    if o is None:
+        o = torch.empty((N, H, d), dtype=dt, device=nq.device)
+    rc = lib.kda_decode_step(_ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
+                             _ptr(cz), _ptr(cbeta), _ptr(accepted), int(W), _ptr(nq), _ptr(nk),
+                             _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(A_log), float(g_min), _ptr(o),
+                             _ptr(err_flag), N, H, d, d, _dtype_code(nq), _stream())
+    _check(rc)
+    return o
+
+
+__all__ = ["kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
+           "kda_default_segments", "kda_decode_step", "load_library", "KDAError",
+           "KDA_COMPUTE_AUTO", "KDA_COMPUTE_F32"]

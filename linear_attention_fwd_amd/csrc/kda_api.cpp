@@ -1,0 +1,225 @@
+// kda_api.cpp -- C ABI of libkda.so: argument validation and kernel launches.
+//
+// Every check that the host can make happens before the first HIP call, so a
+// rejected call enqueues nothing.  No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kD = 128;
+
+// Shared validation of the prefill entry points.
+int check_prefill(const void *q, const void *k, const void *v, const void *g_logits,
+                  const void *beta, float g_min, const int32_t *cu_seqlens,
+                  const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
+                  int32_t dv, int32_t dtype, int32_t compute, const void *o) {
+  if (T > 0 && (!q || !k || !v || !g_logits || !beta || !o))
+    return fail(KDA_ERR_NULL, "q, k, v, g_logits, beta and o must be non-NULL when T > 0");
+  if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported (got %d, %d)", dk, dv);
+  if (H <= 0) return fail(KDA_ERR_SHAPE, "H must be positive (got %d)", H);
+  if (T < 0) return fail(KDA_ERR_SHAPE, "T must be >= 0");
+  if (N <= 0) return fail(KDA_ERR_SHAPE, "N must be >= 1 (got %d)", N);
+  if (T > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "T must fit int32 offsets");
+  if ((int64_t)N * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "N * H too large");
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (compute != KDA_COMPUTE_AUTO && compute != KDA_COMPUTE_F32)
+    return fail(KDA_ERR_DTYPE, "unknown compute mode %d", compute);
+  if (!(g_min >= -5.0f && g_min < 0.0f))
+    return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
+  if (cu_seqlens) {
+    if (!cu_seqlens_host)
+      return fail(KDA_ERR_SEQLENS, "cu_seqlens_host is required with cu_seqlens");
+    if (cu_seqlens_host[0] != 0) return fail(KDA_ERR_SEQLENS, "cu_seqlens[0] must be 0");
+    for (int32_t n = 0; n < N; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(KDA_ERR_SEQLENS, "cu_seqlens must be non-decreasing (at %d)", n);
+    if ((int64_t)cu_seqlens_host[N] != T)
+      return fail(KDA_ERR_SEQLENS, "cu_seqlens[N] = %d but T = %lld", cu_seqlens_host[N], (long long)T);
+  } else if (N != 1) {
+    return fail(KDA_ERR_SEQLENS, "cu_seqlens is required when N > 1");
+  }
+  return KDA_OK;
+}
+
+bool has_empty_doc(const int32_t *cu_host, int32_t N, int64_t T) {
+  if (!cu_host) return T == 0;
+  for (int32_t n = 0; n < N; ++n)
+    if (cu_host[n + 1] == cu_host[n]) return true;
+  return false;
+}
+
+size_t scan_workspace(int64_t n_seg, int64_t H) {
+  return (size_t)n_seg * H * kD * (3 * kD) * sizeof(float);  // pairs [., 2D] + entry [., D]
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_GATE_BOUND: return "KDA_ERR_GATE_BOUND";
+    case KDA_ERR_SEQLENS: return "KDA_ERR_SEQLENS";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}
+
+const char *kda_last_error(void) { return g_err; }
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_logits,
+                  const void *beta, const float *A_log, float g_min,
+                  const float *initial_state, const int32_t *cu_seqlens,
+                  const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                  int32_t dk, int32_t dv, int32_t dtype, int32_t compute, void *o,
+                  float *final_state, void *stream) {
+  int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
+                         dk, dv, dtype, compute, o);
+  if (rc != KDA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    kda::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
+    p.A_log = A_log; p.g_min = g_min;
+    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
+    p.mode = 0; p.n_items = N; p.seg_len = 0;
+    p.item_init = initial_state; p.doc_init = nullptr;
+    p.o = o; p.final_state = final_state;
+    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, compute == KDA_COMPUTE_F32 || dtype == KDA_F32, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd empty documents");
+  }
+  return KDA_OK;
+}
+
+int kda_default_segments(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed");
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return fail(KDA_ERR_HIP, "cannot query the compute-unit count");
+  return cus;
+}
+
+size_t kda_segment_scan_workspace_size(int32_t n_segments, int32_t H, int32_t dk, int32_t dv) {
+  if (n_segments <= 0 || H <= 0 || dk != kD || dv != kD) return 0;
+  return scan_workspace(n_segments, H);
+}
+
+int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_logits,
+                     const void *beta, const float *A_log, float g_min,
+                     const float *initial_state, const int32_t *cu_seqlens,
+                     const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                     int32_t dk, int32_t dv, int32_t dtype, int32_t compute,
+                     int32_t n_segments, void *o, float *final_state, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
+                         dk, dv, dtype, compute, o);
+  if (rc != KDA_OK) return rc;
+  if (final_state && initial_state && final_state == initial_state)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not alias initial_state");
+  int64_t n_seg = n_segments;
+  if (n_seg <= 0) {
+    const int cus = kda_default_segments();
+    if (cus < 0) return cus;
+    n_seg = cus;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    if (n_seg > T) n_seg = T;
+    const int64_t seg_len = (T + n_seg - 1) / n_seg;
+    n_seg = (T + seg_len - 1) / seg_len;  // no empty segment
+    if (n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
+    const size_t need = scan_workspace(n_seg, H);
+    if (!workspace || workspace_bytes < need)
+      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    float *pairs = (float *)workspace;
+    float *entry = pairs + (size_t)n_seg * H * kD * 2 * kD;
+    const bool bf16_in = dtype == KDA_BF16;
+    const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
+
+    kda::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
+    p.A_log = A_log; p.g_min = g_min;
+    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
+    p.n_items = (int)n_seg; p.seg_len = seg_len;
+    p.doc_init = initial_state;
+    // A: segment pairs (M, S~)
+    p.mode = 2; p.item_init = nullptr; p.o = nullptr; p.final_state = pairs;
+    hipError_t e = kda::launch_fwd(p, bf16_in, f32c, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
+    // B: entry states
+    e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, T, H, (int)n_seg, seg_len,
+                              entry, f32c, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
+    // C: re-run every segment from its exact entry state
+    p.mode = 1; p.item_init = entry; p.o = o; p.final_state = final_state;
+    e = kda::launch_fwd(p, bf16_in, f32c, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan empty documents");
+  }
+  return KDA_OK;
+}
+
+int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
+                    const void *cv, const void *cz, const void *cbeta,
+                    const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                    const void *nv, const void *nz, const void *nbeta, const float *A_log,
+                    float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
+                    int32_t dv, int32_t dtype, void *stream) {
+  if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
+  if (N < 0 || H <= 0 || W < 0) return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0");
+  if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "N * H too large");
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (!(g_min >= -5.0f && g_min < 0.0f))
+    return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
+  if (N == 0) return KDA_OK;
+  if (!state || !accepted || !nq || !nk || !nv || !nz || !nbeta || !o)
+    return fail(KDA_ERR_NULL, "state, accepted, bonus inputs and o must be non-NULL");
+  if (W > 0 && (!cq || !ck || !cv || !cz || !cbeta))
+    return fail(KDA_ERR_NULL, "draft caches must be non-NULL when W > 0");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = (dtype == KDA_BF16)
+      ? kda::launch_decode<kda::bf16_t>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq,
+                                        nk, nv, nz, nbeta, A_log, g_min, o, err_flag, N, H, st)
+      : kda::launch_decode<float>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk,
+                                  nv, nz, nbeta, A_log, g_min, o, err_flag, N, H, st);
+  if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// kda_launch.h -- host-side launchers of the KDA kernels (internal to libkda.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef uint16_t bf16_t;  // storage type of bf16 tensors
+
+struct FwdParams {
+  const void *q, *k, *v, *z, *beta;
+  const float *A_log;
+  float g_min;
+  const int32_t *cu;       // [N+1] device document offsets, or nullptr = one document [0, T)
+  int N;
+  int64_t T;
+  int H;
+  int mode;                // 0: items are documents; 1: items are seg_len-token segments
+                           // (re-run from entry states); 2: segment pairs (M, S~)
+  int n_items;
+  int64_t seg_len;
+  const float *item_init;  // mode 0: initial state per document (or nullptr = 0);
+                           // mode 1: entry state per segment [n_items, H, D, D]
+  const float *doc_init;   // modes 1, 2: initial state per document (or nullptr = 0)
+  void *o;                 // mode 0, 1: output [T, H, D]
+  float *final_state;      // modes 0, 1: [N, H, D, D] or nullptr; mode 2: pairs
+                           // [n_items, H, D, 2D] (columns 0..127 = S~, 128..255 = M)
+  int nsplit;              // set by the launcher
+};
+
+hipError_t launch_fwd(FwdParams p, bool bf16_in, bool f32_compute, hipStream_t stream);
+// final_state[d] = initial_state[d] (or 0) for every empty document d;
+// cu == nullptr means one document of T tokens.
+hipError_t launch_copy_empty(const int32_t *cu, int64_t T, const float *init, float *fin, int N,
+                             int H, hipStream_t stream);
+hipError_t launch_pair_scan(const float *pairs, const float *S0, const int32_t *cu, int N,
+                            int64_t T, int H, int n_seg, int64_t seg_len, float *entry,
+                            bool f32_compute, hipStream_t stream);
+
+template <typename Tin>
+hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, const void *ck,
+                         const void *cv, const void *cz, const void *cbeta,
+                         const int32_t *accepted, int W, const void *nq, const void *nk,
+                         const void *nv, const void *nz, const void *nbeta, const float *A_log,
+                         float g_min, void *o, int32_t *err_flag, int N, int H,
+                         hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,137 @@
+// kda_scan.hip -- scan of segment pairs into exact entry states (gfx950).
+//
+// Equation (17) of "Kimi K3 模型结构（7）：结构决定系统" and steps 2-4 of its
+// derivation: a segment maps its entry state E to M E + S~, and the entry
+// state of segment j+1 is E_{j+1} = M_j E_j + S~_j.  Where a document starts
+// exactly on the boundary of segment j the state is reset to that document's
+// own initial state instead (section "文档边界"); documents starting strictly
+// inside a segment are folded into that segment's pair (M = 0) upstream.
+//
+// One workgroup per (head, 16-column slice of the state); columns of E never
+// mix in E <- M E + S~, so slices are independent.  Each of the 4 waves owns
+// 32 rows of E; the current E slice is shared through LDS (transposed so a
+// lane's B operand is one contiguous read).  With bf16 arithmetic the product
+// uses a hi/lo split of both operands (three MFMAs, about 16 mantissa bits),
+// since errors in M E would otherwise propagate along the whole scan; the fp32
+// verification build uses fp32 MFMA.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int SCAN_THREADS = 256;
+
+__device__ __forceinline__ int scan_doc_of(const int32_t *cu, int N, int64_t pos) {
+  if (!cu) return 0;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool F32C>
+__global__ void __launch_bounds__(SCAN_THREADS, 1)
+kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ S0,
+                     const int32_t *__restrict__ cu, int N, int H, int n_seg, int64_t seg_len,
+                     float *__restrict__ entry) {
+  __shared__ __align__(16) float ET[16][D];  // E slice, [column][row]
+
+  const int h = blockIdx.x / 8;
+  const int cs = blockIdx.x % 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int col = 16 * cs + j;
+
+  auto row_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * g + r; };
+  auto load_state = [&](const float *src, floatx4 (&E)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) E[t][r] = src ? src[row_of(t, r) * D + col] : 0.f;
+  };
+  auto publish = [&](int seg, const floatx4 (&E)[2]) {
+    float *dst = entry + ((int64_t)seg * H + h) * (D * D);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dst[row_of(t, r) * D + col] = E[t][r];
+        ET[j][row_of(t, r)] = E[t][r];
+      }
+  };
+  auto doc_state = [&](int d) -> const float * {
+    return S0 ? S0 + ((int64_t)d * H + h) * (D * D) : nullptr;
+  };
+
+  floatx4 E[2];
+  load_state(doc_state(scan_doc_of(cu, N, 0)), E);
+  publish(0, E);
+  __syncthreads();
+
+  for (int s = 1; s < n_seg; ++s) {
+    const int64_t pos = (int64_t)s * seg_len;
+    const int d = scan_doc_of(cu, N, pos);
+    const bool reset = cu ? ((int64_t)cu[d] == pos) : false;
+    if (reset) {
+      load_state(doc_state(d), E);
+    } else {
+      const float *P = pairs + ((int64_t)(s - 1) * H + h) * (D * 2 * D);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        floatx4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = P[row_of(t, r) * (2 * D) + col];  // S~
+        const float *Mrow = P + (32 * w + 16 * t + j) * (2 * D) + D;        // row of M
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 a0 = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g);
+          const float4 a1 = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g + 4);
+          const float4 b0 = *reinterpret_cast<const float4 *>(&ET[j][32 * kb + 8 * g]);
+          const float4 b1 = *reinterpret_cast<const float4 *>(&ET[j][32 * kb + 8 * g + 4]);
+          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          if constexpr (F32C) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(av[e], bv[e], acc);
+          } else {
+            bf16x8 ah, al, bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ah[e] = (__bf16)av[e];
+              al[e] = (__bf16)(av[e] - (float)ah[e]);
+              bh[e] = (__bf16)bv[e];
+              bl[e] = (__bf16)(bv[e] - (float)bh[e]);
+            }
+            acc = mfma_bf16_k32(al, bh, acc);
+            acc = mfma_bf16_k32(ah, bl, acc);
+            acc = mfma_bf16_k32(ah, bh, acc);
+          }
+        }
+        E[t] = acc;
+      }
+    }
+    __syncthreads();  // every wave has read the previous E slice
+    publish(s, E);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_pair_scan(const float *pairs, const float *S0, const int32_t *cu, int N,
+                            int64_t /*T*/, int H, int n_seg, int64_t seg_len, float *entry,
+                            bool f32_compute, hipStream_t stream) {
+  const dim3 grid((unsigned)(H * 8));
+  if (f32_compute)
+    hipLaunchKernelGGL(kda_pair_scan_kernel<true>, grid, dim3(SCAN_THREADS), 0, stream, pairs,
+                       S0, cu, N, H, n_seg, seg_len, entry);
+  else
+    hipLaunchKernelGGL(kda_pair_scan_kernel<false>, grid, dim3(SCAN_THREADS), 0, stream, pairs,
+                       S0, cu, N, H, n_seg, seg_len, entry);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,116 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and the
+CPU oracle on the same seeded inputs, and compare them."""
+from __future__ import annotations
+
+import numpy as np
+
+import kda_gen
+import oracle
+
+# Tolerances (max relative L2 error per (document, head) slice, O and final state):
+# bf16-MFMA arithmetic 1e-2; fp32 verification arithmetic 1e-4.
+TOL_BF16 = 1e-2
+TOL_F32 = 1e-4
+# Storing an output in bf16 (round to nearest even) alone contributes a relative
+# error of at most 2^-8 per element, so an fp32-arithmetic run on bf16 inputs is
+# held to 1e-4 on the fp32 states and to 2^-8 + 1e-4 on its bf16 outputs.
+TOL_BF16_STORAGE = 2.0 ** -8
+
+
+def rel_l2_slices(x, ref, cu=None, axis_tokens=True):
+    """Max and global relative L2 error.  For outputs [T, H, D] the slices are
+    (document, head); for states [N, H, D, D] they are (document, head)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    worst = 0.0
+    if axis_tokens:
+        T, H = ref.shape[:2]
+        bounds = [(0, T)] if cu is None else list(zip(cu[:-1], cu[1:]))
+        for s, e in bounds:
+            if e <= s:
+                continue
+            for h in range(H):
+                den = np.linalg.norm(ref[s:e, h])
+                if den > 0:
+                    worst = max(worst, np.linalg.norm(x[s:e, h] - ref[s:e, h]) / den)
+    else:
+        N, H = ref.shape[:2]
+        for n in range(N):
+            for h in range(H):
+                den = np.linalg.norm(ref[n, h])
+                if den > 0:
+                    worst = max(worst, np.linalg.norm(x[n, h] - ref[n, h]) / den)
+    glob = np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300)
+    return worst, glob
+
+
+def oracle_forward(inp, heads=None, group=8):
+    """Oracle on a PrefillInputs, optionally on a subset of heads, in head groups
+    to bound the fp64 working set."""
+    heads = list(range(inp.H)) if heads is None else list(heads)
+    T = inp.T
+    o = np.zeros((T, len(heads), 128))
+    S = np.zeros((inp.N, len(heads), 128, 128))
+    for g0 in range(0, len(heads), group):
+        hs = heads[g0:g0 + group]
+        z = inp.z.f32()[:, hs].astype(np.float64)
+        gg = oracle.gate(z, inp.A_log[hs], inp.g_min)
+        del z
+        S0 = None if inp.S0 is None else inp.S0[:, hs].astype(np.float64)
+        oo, SS = oracle.recurrent(inp.q.f32()[:, hs], inp.k.f32()[:, hs], inp.v.f32()[:, hs], gg,
+                                  inp.beta.f32()[:, hs], S0, inp.cu_seqlens)
+        o[:, g0:g0 + len(hs)] = oo
+        S[:, g0:g0 + len(hs)] = SS
+    return o, S
+
+
+def gpu_inputs(inp, device="cuda"):
+    import torch
+    t = {name: kda_gen.to_torch(getattr(inp, name), device) for name in ("q", "k", "v", "z", "beta")}
+    t["A_log"] = torch.from_numpy(inp.A_log).to(device)
+    t["S0"] = None if inp.S0 is None else torch.from_numpy(inp.S0).to(device)
+    t["cu"] = torch.from_numpy(inp.cu_seqlens).to(device) if inp.N > 1 else None
+    t["cu_host"] = inp.cu_seqlens if inp.N > 1 else None
+    return t
+
+
+def gpu_chunk_fwd(inp, compute=0, t=None):
+    import linear_attention_fwd_amd as kda
+    import torch
+    t = t or gpu_inputs(inp)
+    o, S = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min,
+                             t["S0"], t["cu"], t["cu_host"], compute=compute)
+    torch.cuda.synchronize()
+    return kda_gen.from_torch(o), kda_gen.from_torch(S)
+
+
+def gpu_segment_scan(inp, n_segments=0, compute=0, t=None):
+    import linear_attention_fwd_amd as kda
+    import torch
+    t = t or gpu_inputs(inp)
+    o, S = kda.kda_segment_scan(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
+                                inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                n_segments=n_segments, compute=compute)
+    torch.cuda.synchronize()
+    return kda_gen.from_torch(o), kda_gen.from_torch(S)
+
+
+def decode_gpu_inputs(inp, device="cuda"):
+    import torch
+    t = {name: kda_gen.to_torch(getattr(inp, name), device)
+         for name in ("cq", "ck", "cv", "cz", "cbeta", "nq", "nk", "nv", "nz", "nbeta")}
+    t["A_log"] = torch.from_numpy(inp.A_log).to(device)
+    t["accepted"] = torch.from_numpy(inp.accepted).to(device)
+    t["state"] = torch.from_numpy(inp.state).to(device)
+    return t
+
+
+def gpu_decode(inp, t=None, state_slots=None, err_flag=None):
+    import linear_attention_fwd_amd as kda
+    import torch
+    t = t or decode_gpu_inputs(inp)
+    o = kda.kda_decode_step(t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"],
+                            t["accepted"], t["nq"], t["nk"], t["nv"], t["nz"], t["nbeta"],
+                            t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
+    torch.cuda.synchronize()
+    return kda_gen.from_torch(o), kda_gen.from_torch(t["state"])

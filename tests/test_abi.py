@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libkda.so loads and exports every function include/kda.h declares;
+* invalid arguments are rejected with the documented status before any HIP
+  call (so nothing here touches a device: every call below fails validation).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_fwd_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, -1, -2, -3
+KDA_ERR_GATE_BOUND, KDA_ERR_SEQLENS, KDA_ERR_WORKSPACE = -4, -5, -6
+KDA_ERR_UNSUPPORTED = -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from linear_attention_fwd_amd import _build
+        _build.build()
+    return kda.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kda_chunk_fwd", "kda_segment_scan", "kda_decode_step"):
+        assert required in names
+    assert set(names) == set(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(kda_[a-z_0-9]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(-4) == b"KDA_ERR_GATE_BOUND"
+    assert lib.kda_status_string(12345) == b"KDA_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _prefill(lib, fn="kda_chunk_fwd", **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A=None, g_min=-5.0, S0=None, cu=None,
+             cu_host=None, N=1, T=128, H=4, dk=128, dv=128, dtype=1, compute=0, o=FAKE,
+             fin=FAKE, nseg=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    args = [a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["g_min"], a["S0"], a["cu"],
+            a["cu_host"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"], a["compute"]]
+    if fn == "kda_chunk_fwd":
+        return lib.kda_chunk_fwd(*args, a["o"], a["fin"], None)
+    return lib.kda_segment_scan(*args, a["nseg"], a["o"], a["fin"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_segment_scan"])
+def test_prefill_validation(lib, fn):
+    assert _prefill(lib, fn, q=None) == KDA_ERR_NULL
+    assert _prefill(lib, fn, o=None) == KDA_ERR_NULL
+    assert _prefill(lib, fn, dk=64) == KDA_ERR_SHAPE
+    assert _prefill(lib, fn, dv=256) == KDA_ERR_SHAPE
+    assert _prefill(lib, fn, H=0) == KDA_ERR_SHAPE
+    assert _prefill(lib, fn, T=-1) == KDA_ERR_SHAPE
+    assert _prefill(lib, fn, dtype=7) == KDA_ERR_DTYPE
+    assert _prefill(lib, fn, compute=3) == KDA_ERR_DTYPE
+    # the subtile factors need 16 * |g_min| < 88: g_min below -5 is refused
+    assert _prefill(lib, fn, g_min=-5.5) == KDA_ERR_GATE_BOUND
+    assert _prefill(lib, fn, g_min=0.0) == KDA_ERR_GATE_BOUND
+    assert _prefill(lib, fn, g_min=float("nan")) == KDA_ERR_GATE_BOUND
+    # N > 1 needs offsets; offsets need a host copy, start at 0, increase, end at T
+    assert _prefill(lib, fn, N=2) == KDA_ERR_SEQLENS
+    good = (ctypes.c_int32 * 3)(0, 50, 128)
+    assert _prefill(lib, fn, N=2, cu=FAKE) == KDA_ERR_SEQLENS
+    for bad in ((1, 50, 128), (0, 90, 60), (0, 50, 127)):
+        arr = (ctypes.c_int32 * 3)(*bad)
+        assert _prefill(lib, fn, N=2, cu=FAKE, cu_host=ctypes.cast(arr, ctypes.c_void_p)) \
+            == KDA_ERR_SEQLENS
+    assert good[2] == 128
+
+
+def test_segment_scan_workspace_checks(lib):
+    # explicit segment count: a short or missing workspace is refused before any launch
+    need = lib.kda_segment_scan_workspace_size(4, 4, 128, 128)
+    assert need == 4 * 4 * 128 * 384 * 4
+    assert lib.kda_segment_scan_workspace_size(0, 4, 128, 128) == 0
+    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=None, ws_bytes=0) == KDA_ERR_WORKSPACE
+    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=FAKE, ws_bytes=need - 1) == KDA_ERR_WORKSPACE
+    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=ctypes.c_void_p(0x1004), ws_bytes=need) \
+        == KDA_ERR_WORKSPACE
+    assert _prefill(lib, "kda_segment_scan", nseg=4, S0=FAKE, fin=FAKE, ws=FAKE,
+                    ws_bytes=need) == KDA_ERR_UNSUPPORTED
+
+
+def test_decode_validation(lib):
+    def call(**kw):
+        a = dict(state=FAKE, slots=None, c=FAKE, acc=FAKE, W=4, n=FAKE, A=None, g_min=-5.0,
+                 o=FAKE, err=None, N=8, H=4, dk=128, dv=128, dtype=1)
+        a.update(kw)
+        c, n = a["c"], a["n"]
+        return lib.kda_decode_step(a["state"], a["slots"], c, c, c, c, c, a["acc"], a["W"], n, n,
+                                   n, n, n, a["A"], a["g_min"], a["o"], a["err"], a["N"], a["H"],
+                                   a["dk"], a["dv"], a["dtype"], None)
+    assert call(state=None) == KDA_ERR_NULL
+    assert call(acc=None) == KDA_ERR_NULL
+    assert call(n=None) == KDA_ERR_NULL
+    assert call(c=None) == KDA_ERR_NULL          # drafts needed when W > 0
+    assert call(dk=64) == KDA_ERR_SHAPE
+    assert call(W=-1) == KDA_ERR_SHAPE
+    assert call(H=0) == KDA_ERR_SHAPE
+    assert call(dtype=5) == KDA_ERR_DTYPE
+    assert call(g_min=-6.0) == KDA_ERR_GATE_BOUND
+    assert call(N=0) == KDA_OK                   # nothing to do, nothing launched
+    assert lib.kda_last_error() is not None

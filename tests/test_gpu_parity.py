@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes here run in seconds on the oracle and still span several chunks, ragged
+tails, empty documents and the gate's extreme regimes.  The full workloads are
+in test_gpu_workloads.py.  Tolerance: max relative L2 error per (document,
+head) slice of O and of the final state, 1e-2 for bf16-MFMA arithmetic and
+1e-4 for the fp32 verification arithmetic.
+"""
+import numpy as np
+import pytest
+
+import kda_gen
+from kda_testlib import (TOL_BF16, TOL_BF16_STORAGE, TOL_F32, gpu_chunk_fwd, gpu_decode, gpu_segment_scan,
+                         decode_gpu_inputs, oracle_forward, rel_l2_slices)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(inp, compute):
+    print(f"[case] T={inp.T} H={inp.H} N={inp.N} dtype={inp.dtype} compute={compute}", flush=True)
+
+
+def _tols(inp, compute):
+    """(tolerance on O, tolerance on the final state)."""
+    if inp.dtype == "f32" or compute == 1:
+        o_tol = TOL_F32 if inp.dtype == "f32" else TOL_F32 + TOL_BF16_STORAGE
+        return o_tol, TOL_F32
+    return TOL_BF16, TOL_BF16
+
+
+def _check_prefill(inp, o, S, tols, ref=None):
+    o_ref, S_ref = ref if ref is not None else oracle_forward(inp)
+    eo, go = rel_l2_slices(o, o_ref, inp.cu_seqlens)
+    es, gs = rel_l2_slices(S, S_ref, axis_tokens=False)
+    print(f"    O: max {eo:.3e} global {go:.3e} | S: max {es:.3e} global {gs:.3e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    assert eo <= tols[0], eo
+    assert es <= tols[1], es
+    return eo, es
+
+
+PREFILL_CASES = {
+    # name: (generator kwargs)
+    "tiny_fp32_workload": dict(seed=0, T=256, H=2, dtype="f32", A_std=0.0),
+    "ragged_tail_bf16": dict(seed=21, T=300, H=4, dtype="bf16", s0_std=0.02, s0_docs="all"),
+    "single_token": dict(seed=22, T=1, H=3, dtype="bf16", s0_std=0.02, s0_docs="all"),
+    "slow_decay_long_memory": dict(seed=23, T=700, H=2, dtype="bf16", z_mean=-6.0,
+                                   s0_std=0.05, s0_docs="all"),
+    "decay_near_bound": dict(seed=24, T=256, H=2, dtype="bf16", z_mean=8.0),
+    "varlen_with_empty_docs": dict(seed=25, T=400, H=3, dtype="bf16",
+                                   lengths=[5, 0, 130, 64, 1, 200, 0], s0_std=0.02,
+                                   s0_docs="all"),
+    "varlen_fp32": dict(seed=26, T=333, H=2, dtype="f32", lengths=[100, 0, 64, 169],
+                        s0_std=0.1, s0_docs="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_chunk_fwd_matches_oracle(name):
+    kw = dict(PREFILL_CASES[name])
+    seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
+    inp = kda_gen.make_prefill(seed, T, H, **kw)
+    ref = oracle_forward(inp)
+    for compute in ((0,) if inp.dtype == "f32" else (0, 1)):
+        _case(inp, compute)
+        o, S = gpu_chunk_fwd(inp, compute=compute)
+        _check_prefill(inp, o, S, _tols(inp, compute), ref)
+
+
+def test_chunk_fwd_is_deterministic():
+    inp = kda_gen.make_prefill(31, 500, 4, "bf16", s0_std=0.02, s0_docs="all")
+    o1, S1 = gpu_chunk_fwd(inp)
+    o2, S2 = gpu_chunk_fwd(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_chunk_fwd_resume_equals_one_call():
+    """Splitting a document at a chunk-aligned token and carrying the final
+    state gives the one-call result (the chunking is then identical)."""
+    inp = kda_gen.make_prefill(32, 384, 2, "bf16", s0_std=0.02, s0_docs="all")
+    o_all, S_all = gpu_chunk_fwd(inp)
+    cut = 192
+    a = kda_gen.PrefillInputs(*(kda_gen.Tensor(x.data[:cut], x.dtype) for x in
+                                (inp.q, inp.k, inp.v, inp.z, inp.beta)), inp.A_log, inp.S0,
+                              np.array([0, cut], np.int32), inp.g_min, inp.dtype)
+    oa, Sa = gpu_chunk_fwd(a)
+    b = kda_gen.PrefillInputs(*(kda_gen.Tensor(x.data[cut:], x.dtype) for x in
+                                (inp.q, inp.k, inp.v, inp.z, inp.beta)), inp.A_log,
+                              Sa.astype(np.float32), np.array([0, inp.T - cut], np.int32),
+                              inp.g_min, inp.dtype)
+    ob, Sb = gpu_chunk_fwd(b)
+    assert np.array_equal(np.concatenate([oa, ob]), o_all)
+    assert np.array_equal(Sb, S_all)
+
+
+SCAN_CASES = {
+    # lengths chosen so that segment boundaries fall inside documents, exactly on
+    # a document start (n_seg=7 -> segments of 215 tokens; a document starts at 430),
+    # and segments contain several document starts
+    "varlen_bf16": dict(seed=41, T=1505, H=2, dtype="bf16",
+                        lengths=[100, 330, 0, 700, 3, 2, 370], s0_std=0.05, s0_docs="all"),
+    "single_doc_fp32": dict(seed=42, T=900, H=2, dtype="f32", s0_std=0.1, s0_docs="all"),
+    "slow_decay_single_doc": dict(seed=43, T=1300, H=2, dtype="bf16", z_mean=-6.0,
+                                  s0_std=0.05, s0_docs="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCAN_CASES))
+@pytest.mark.parametrize("n_seg", [1, 7, 64])
+def test_segment_scan_matches_oracle(name, n_seg):
+    kw = dict(SCAN_CASES[name])
+    seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
+    inp = kda_gen.make_prefill(seed, T, H, **kw)
+    ref = oracle_forward(inp)
+    for compute in ((0,) if inp.dtype == "f32" else (0, 1)):
+        _case(inp, compute)
+        print(f"    n_segments={n_seg}", flush=True)
+        o, S = gpu_segment_scan(inp, n_segments=n_seg, compute=compute)
+        _check_prefill(inp, o, S, _tols(inp, compute), ref)
+
+
+def test_segment_scan_one_segment_equals_chunk_fwd():
+    inp = kda_gen.make_prefill(44, 640, 2, "bf16", lengths=[200, 440], s0_std=0.02,
+                               s0_docs="all")
+    o1, S1 = gpu_chunk_fwd(inp)
+    o2, S2 = gpu_segment_scan(inp, n_segments=1)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+# ---------------------------------------------------------------------------
+# decode with speculative-verify replay
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_matches_oracle(dtype):
+    inp = kda_gen.make_decode(51, N=40, H=4, W=4, dtype=dtype,
+                              accepted=[i % 5 for i in range(40)])
+    print(f"[case] decode N={inp.N} H={inp.H} W={inp.W} dtype={dtype}", flush=True)
+    o_ref, S_ref = oracle.decode(inp)
+    o, S = gpu_decode(inp)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    print(f"    o: {eo:.3e}  state: {es:.3e}", flush=True)
+    # fp32 arithmetic throughout: the state matches to fp32 accuracy; o is stored
+    # in the input dtype (bf16 rounding alone is ~2e-3 relative)
+    assert es <= TOL_F32
+    assert eo <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def test_decode_slots_and_clamping():
+    import torch
+    inp = kda_gen.make_decode(52, N=6, H=2, W=4, dtype="bf16", accepted=[0, 4, 7, -1, 2, 3])
+    t = decode_gpu_inputs(inp)
+    # a state pool twice as large, sequences scattered into it
+    slots = np.array([9, 0, 4, 11, 6, 2], dtype=np.int32)
+    pool = np.zeros((12, inp.H, 128, 128), np.float32)
+    pool[slots] = inp.state
+    t["state"] = torch.from_numpy(pool).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, P = gpu_decode(inp, t=t, state_slots=torch.from_numpy(slots).cuda(), err_flag=err)
+    assert int(err.item()) == 1  # 7 and -1 were out of range
+    clamped = kda_gen.make_decode(52, N=6, H=2, W=4, dtype="bf16", accepted=[0, 4, 4, 0, 2, 3])
+    o_ref, S_ref = oracle.decode(clamped)
+    es, _ = rel_l2_slices(P[slots], S_ref, axis_tokens=False)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    assert es <= TOL_F32 and eo <= TOL_BF16
+    untouched = np.setdiff1d(np.arange(12), slots)
+    assert np.all(P[untouched] == 0)
+
+
+def test_decode_equals_chunk_fwd_on_the_same_tokens():
+    """A replay of a accepted drafts + bonus equals a prefill over those a+1 tokens
+    from the saved state (two independent GPU paths)."""
+    inp = kda_gen.make_decode(53, N=5, H=2, W=4, dtype="f32", accepted=[4, 4, 4, 4, 4])
+    o_dec, S_dec = gpu_decode(inp)
+    n = 3
+    toks = lambda c, nb: np.concatenate([c.data[n], nb.data[n][None]])
+    pre = kda_gen.PrefillInputs(
+        kda_gen.Tensor(toks(inp.cq, inp.nq), "f32"), kda_gen.Tensor(toks(inp.ck, inp.nk), "f32"),
+        kda_gen.Tensor(toks(inp.cv, inp.nv), "f32"), kda_gen.Tensor(toks(inp.cz, inp.nz), "f32"),
+        kda_gen.Tensor(np.concatenate([inp.cbeta.data[n], inp.nbeta.data[n][None]]), "f32"),
+        inp.A_log, inp.state[n:n + 1], np.array([0, 5], np.int32), inp.g_min, "f32")
+    o_pre, S_pre = gpu_chunk_fwd(pre)
+    assert rel_l2_slices(S_dec[n:n + 1], S_pre, axis_tokens=False)[0] < 1e-5
+    assert np.linalg.norm(o_dec[n] - o_pre[-1]) / np.linalg.norm(o_pre[-1]) < 1e-5
