@@ -21,6 +21,10 @@ namespace kda {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+// fp32 -> bf16 (round to nearest even), two values per v_cvt_pk_bf16_f32
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) { return __builtin_convertvector(x, bf16x4); }
+__device__ __forceinline__ bf16x8 to_bf16x8(floatx8 x) { return __builtin_convertvector(x, bf16x8); }
 typedef uint16_t bf16_t;  // storage type of bf16 tensors in global memory
 
 constexpr int D = 128;       // d_k = d_v
@@ -120,59 +124,141 @@ template <> struct io<bf16_t> {
   static __device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(*p); }
   static __device__ __forceinline__ void store1(bf16_t *p, float v) { *p = f32_to_bf16(v); }
   static __device__ __forceinline__ void store4(bf16_t *p, const float *x) {
-    uint2 w;
-    w.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
-    *reinterpret_cast<uint2 *>(p) = w;
+    *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(floatx4{x[0], x[1], x[2], x[3]});
   }
 };
 
-// ---- buffer-resource access -------------------------------------------------
-// Raw buffer loads/stores split an address into a per-lane VGPR offset and a
-// wave-uniform SGPR offset.  The kernels keep 128 x 128 state tiles in MFMA
-// accumulator layout; with plain pointers every element's 64-bit address is a
-// separate loop-invariant value the compiler hoists and keeps live, with buffer
-// access only one lane offset stays in a VGPR.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
-  // stride 0, full 31-bit range, gfx9 raw-buffer data format word
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7FFFFFFF, 0x00020000);
+// ---- wave-uniform values ------------------------------------------------------
+// Values the compiler cannot prove uniform (loaded through vector memory) are
+// re-read from the first lane, so buffer descriptors built from them stay in
+// SGPRs instead of being wrapped in per-lane loops.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-__device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, float x, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+template <typename T> __device__ __forceinline__ T *uniptr(T *p) {
+  return reinterpret_cast<T *>((uintptr_t)uni64((int64_t)(uintptr_t)p));
 }
 
-// A 128-row state slice in accumulator layout: tile[m][n][r] is row
-// 16m + 4g + r, column col0 + 16n + j of a row-major matrix with `ld` columns.
+// ---- buffer-resource access -------------------------------------------------
+// Raw buffer loads/stores take a per-lane VGPR offset from a wave-uniform base.
+// `bytes` bounds the descriptor: loads past it return 0 and stores past it are
+// dropped, which masks ragged chunk tails without branches.  All offsets used
+// here go into the VGPR operand (the range check covers it).
+// The base and size must be wave-uniform; they are re-read from the first lane
+// so the descriptor is built in SGPRs even when they reach here through a
+// branch merge the compiler cannot prove uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  // stride 0, gfx9 raw-buffer data format word
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(uniptr(base)), 0, uni(bytes), 0x00020000);
+}
+__device__ __forceinline__ float buf_ld_f32(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, float x, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct bufio;
+template <> struct bufio<float> {
+  static constexpr int ES = 4;
+  struct raw8 { u32x4 a, b; };
+  typedef uint32_t raw1;
+  static __device__ __forceinline__ raw8 ld8(__amdgpu_buffer_rsrc_t r, int voff) {
+    return raw8{__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0),
+                __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0)};
+  }
+  static __device__ __forceinline__ void cvt8(const raw8 &x, float *y) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { y[i] = __uint_as_float(x.a[i]); y[4 + i] = __uint_as_float(x.b[i]); }
+  }
+  static __device__ __forceinline__ raw1 ld1(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+  }
+  static __device__ __forceinline__ float cvt1(raw1 x) { return __uint_as_float(x); }
+  static __device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, float x, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
+  }
+};
+template <> struct bufio<bf16_t> {
+  static constexpr int ES = 2;
+  struct raw8 { u32x4 a; };
+  typedef unsigned short raw1;
+  static __device__ __forceinline__ raw8 ld8(__amdgpu_buffer_rsrc_t r, int voff) {
+    return raw8{__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0)};
+  }
+  static __device__ __forceinline__ void cvt8(const raw8 &x, float *y) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[2 * i] = __uint_as_float(x.a[i] << 16);
+      y[2 * i + 1] = __uint_as_float(x.a[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ raw1 ld1(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+  }
+  static __device__ __forceinline__ float cvt1(raw1 x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ void st1(__amdgpu_buffer_rsrc_t r, float x, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, voff, 0, 0);
+  }
+};
+
+// A 128-row state slice in accumulator layout: tile[m][n][r] is row 16m + 4g + r,
+// column col0 + 16n + j of a row-major fp32 matrix with `ld` columns at `base`
+// (a wave-uniform pointer).
 template <int NT>
 __device__ __forceinline__ void state_load(floatx4 (&S)[8][NT], const float *base, int ld,
                                            int col0, int g, int j) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, D * ld * 4);
   const int voff = (4 * g * ld + col0 + j) * 4;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][n][e] = buf_ld_f32(r, voff, ((16 * m + e) * ld + 16 * n) * 4);
+      for (int e = 0; e < 4; ++e) S[m][n][e] = buf_ld_f32(r, voff + ((16 * m + e) * ld + 16 * n) * 4);
 }
 template <int NT>
 __device__ __forceinline__ void state_store(const floatx4 (&S)[8][NT], float *base, int ld,
                                             int col0, int g, int j) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, D * ld * 4);
   const int voff = (4 * g * ld + col0 + j) * 4;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) buf_st_f32(r, S[m][n][e], voff, ((16 * m + e) * ld + 16 * n) * 4);
+      for (int e = 0; e < 4; ++e) buf_st_f32(r, S[m][n][e], voff + ((16 * m + e) * ld + 16 * n) * 4);
 }
 
-// Bounded gate of equation (5) ("序列维度（下）", section "K3 的改动：下界衰减"):
-// g = g_min * sigmoid(exp(A_h) * z).  `escale` = exp(A_h) is precomputed.
+// ---- XOR-swizzled LDS tiles -------------------------------------------------
+// Row-major tile with COLS elements of E per row.  The 16-byte chunk c of row r
+// is stored at chunk c ^ sw(r), so that the 16 rows an MFMA operand read touches
+// at one column fall into distinct banks.
+template <typename E, int COLS> struct Tile {
+  static constexpr int EPC = 16 / (int)sizeof(E);          // elements per 16-byte chunk
+  static constexpr int NCH = COLS / EPC;                    // chunks per row
+  static __device__ __forceinline__ int sw(int r) {
+    return NCH >= 16 ? (r & 15) : ((r >> 1) & (NCH - 1));
+  }
+  // element offset of logical (r, col); an access of up to one chunk starting at
+  // col must not cross a chunk boundary
+  static __device__ __forceinline__ int idx(int r, int col) {
+    return r * COLS + (((col / EPC) ^ sw(r)) * EPC) + (col % EPC);
+  }
+};
+
+// Bounded gate of equation (5) ("序列维度（下）", section "K3 的改动：下界衰减"),
+// g = g_min * sigmoid(exp(A_h) z), returned in base-2 units (g * log2 e) so the
+// decay factors are plain exp2.  c1 = -exp(A_h) * log2 e and gm = g_min * log2 e
+// are precomputed; gm = 0 turns a padding row into "no decay".
+__device__ __forceinline__ float kda_gate2(float z, float c1, float gm) {
+  return gm * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(c1 * z));
+}
+// The same gate in natural-log units (decode path).
 __device__ __forceinline__ float kda_gate(float z, float escale, float g_min) {
   const float x = escale * z;
   return g_min * __builtin_amdgcn_rcpf(1.0f + __expf(-x));

@@ -44,6 +44,12 @@ def rel_l2_slices(x, ref, cu=None, axis_tokens=True):
     return worst, glob
 
 
+def _slice_f32(t, hs):
+    """fp32 values of heads hs of a kda_gen.Tensor [T, H, ...], converting only the slice."""
+    x = t.data[:, hs]
+    return x.astype(np.float32) if t.dtype == "f32" else kda_gen.bf16_bits_to_f32(x)
+
+
 def oracle_forward(inp, heads=None, group=8):
     """Oracle on a PrefillInputs, optionally on a subset of heads, in head groups
     to bound the fp64 working set."""
@@ -53,12 +59,11 @@ def oracle_forward(inp, heads=None, group=8):
     S = np.zeros((inp.N, len(heads), 128, 128))
     for g0 in range(0, len(heads), group):
         hs = heads[g0:g0 + group]
-        z = inp.z.f32()[:, hs].astype(np.float64)
-        gg = oracle.gate(z, inp.A_log[hs], inp.g_min)
-        del z
+        gg = oracle.gate(_slice_f32(inp.z, hs).astype(np.float64), inp.A_log[hs], inp.g_min)
         S0 = None if inp.S0 is None else inp.S0[:, hs].astype(np.float64)
-        oo, SS = oracle.recurrent(inp.q.f32()[:, hs], inp.k.f32()[:, hs], inp.v.f32()[:, hs], gg,
-                                  inp.beta.f32()[:, hs], S0, inp.cu_seqlens)
+        oo, SS = oracle.recurrent(_slice_f32(inp.q, hs), _slice_f32(inp.k, hs),
+                                  _slice_f32(inp.v, hs), gg, _slice_f32(inp.beta, hs), S0,
+                                  inp.cu_seqlens)
         o[:, g0:g0 + len(hs)] = oo
         S[:, g0:g0 + len(hs)] = SS
     return o, S
