@@ -26,7 +26,8 @@ KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
-EXPORTS = ("kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_segment_scan",
+           "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_status_string", "kda_last_error")
 
 _lib = None
@@ -48,8 +49,10 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
-    lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp]
+    lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_segment_scan.argtypes = prefill + [i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_segment_scan.restype = ctypes.c_int
     lib.kda_segment_scan_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -141,13 +144,20 @@ def _prefill_common(q, k, v, g_logits, beta, A_log, initial_state, cu_seqlens, c
     return T, H, dk, dv, N, cu_dev, cu_host
 
 
+def kda_chunk_fwd_workspace_size(N: int, T: int, H: int, dk: int = 128, dv: int = 128) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_size(N, T, H, dk, dv))
+
+
 def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                   initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, compute: int = KDA_COMPUTE_AUTO,
-                  o=None, final_state=None) -> Tuple[object, Optional[object]]:
+                  o=None, final_state=None, workspace=None) -> Tuple[object, Optional[object]]:
     """Chunkwise KDA prefill.  q, k, v, g_logits: [T, H, 128]; beta: [T, H] (same
     dtype, bf16 or fp32); A_log: [H] fp32 or None; initial_state: [N, H, 128, 128]
     fp32 or None; cu_seqlens: [N+1] int32 (device and/or host copy).
+    workspace: None allocates one (uint8, kda_chunk_fwd_workspace_size bytes) when
+    the two-kernel path applies (bf16 inputs, compute AUTO); False runs the fused
+    single kernel; a uint8 device tensor is used as given.
     Returns (o [T, H, 128] in the input dtype, final_state [N, H, 128, 128] fp32 or None)."""
     torch = _torch()
     lib = load_library()
@@ -157,11 +167,17 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        split = _dtype_code(q) == KDA_BF16 and int(compute) == KDA_COMPUTE_AUTO and T > 0
+        workspace = (torch.empty(kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
+                                 device=q.device) if split else False)
+    ws_ptr, ws_bytes = (None, 0) if workspace is False else \
+        (_ptr(workspace), workspace.numel() * workspace.element_size())
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                            float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
                            dk, dv, _dtype_code(q), int(compute), _ptr(o), _ptr(final_state),
-                           _stream())
+                           ws_ptr, ws_bytes, _stream())
     _check(rc)
     return o, final_state
 

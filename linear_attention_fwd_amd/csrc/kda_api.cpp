@@ -100,12 +100,31 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                   const float *initial_state, const int32_t *cu_seqlens,
                   const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
                   int32_t dk, int32_t dv, int32_t dtype, int32_t compute, void *o,
-                  float *final_state, void *stream) {
+                  float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
                          dk, dv, dtype, compute, o);
   if (rc != KDA_OK) return rc;
+  const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
+  const bool split = workspace != nullptr && !f32c;
+  if (split && T > 0) {
+    const size_t need = kda::split_workspace_bytes(T, N, H);
+    if (workspace_bytes < need)
+      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (kda::n_chunk_slots(T, N) * H > (int64_t)INT32_MAX)
+      return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
+  }
   hipStream_t st = (hipStream_t)stream;
-  if (T > 0) {
+  if (T > 0 && split) {
+    kda::SplitParams p{};
+    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
+    p.A_log = A_log; p.g_min = g_min;
+    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
+    p.init = initial_state; p.o = o; p.final_state = final_state;
+    p.ws = workspace; p.n_slots = kda::n_chunk_slots(T, N);
+    hipError_t e = kda::launch_split(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
+  } else if (T > 0) {
     kda::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
     p.A_log = A_log; p.g_min = g_min;
@@ -113,7 +132,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
     p.mode = 0; p.n_items = N; p.seg_len = 0;
     p.item_init = initial_state; p.doc_init = nullptr;
     p.o = o; p.final_state = final_state;
-    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, compute == KDA_COMPUTE_F32 || dtype == KDA_F32, st);
+    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, f32c, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
@@ -121,6 +140,11 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd empty documents");
   }
   return KDA_OK;
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv) {
+  if (N <= 0 || T < 0 || H <= 0 || dk != kD || dv != kD) return 0;
+  return kda::split_workspace_bytes(T, N, H);
 }
 
 int kda_default_segments(void) {

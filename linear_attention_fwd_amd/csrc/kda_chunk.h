@@ -1,0 +1,536 @@
+// kda_chunk.h -- stages of the per-chunk prep shared by the chunk kernels.
+//
+// A chunk is C = 64 tokens of one head, worked on by one workgroup of four
+// waves.  Thread layout of the token-parallel stages: wave w owns subtile w
+// (tokens 16w..16w+15); lane (tq, cg) holds tokens 16w + 4tq + r (r = 0..3),
+// channels 8cg..8cg+7.  The stages, in the order the kernels call them:
+//
+//   a1  prep_gate_cumsum     gate g = g_min*sigmoid(exp(A_h) z) and the
+//       in-chunk inclusive cumulative log-decay G ("序列维度（下）", eq. (3),
+//       eq. (5), section "数值问题"), in base-2 units;
+//   a2  prep_decay_operands  the decay factors Q_decay = e^G q, K_decay =
+//       e^G k, K_restore = e^(G_C - G) k and the 16-token subtile operands
+//       referenced to the first token s of the query subtile: e^(G_i - G_s)
+//       <= 1 on the query side, e^(G_s - G_j) < e^75 on the key side (g >
+//       g_min = -5 keeps it inside the bf16 range, section "K3 的改动：下界衰减");
+//   a3  prep_subtile_products  L = StrictTril(Diag(beta) K_decay K_inv^T) and
+//       M_qk = Tril(Q_decay K_inv^T) (diagonal kept) per 16x16 subtile pair on
+//       MFMA (SemiAnalysis page, section "FlashKDA 算法");
+//   a4  prep_diag_inverse + prep_block_columns  the UT transform INV =
+//       (I + L)^-1 ("序列维度（下）", section "UT 变换"): each 16x16 diagonal
+//       block by repeated squaring, (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8),
+//       then one block column per wave, X_IJ = -T_II sum_K L_IK X_KJ, stored as
+//       INV Diag(beta).
+//
+// Where a stage's result goes (LDS for the fused kernel, the chunk image in
+// global memory for the split prep kernel) is the caller's choice: a2 and a3
+// hand their recurrence operands to a sink functor.
+#pragma once
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int FWD_THREADS = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Keep the instruction scheduler from moving work across chunk phases.
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// ---------------------------------------------------------------------------
+// MFMA operand plumbing for the two arithmetic modes.  Operand reads take a
+// tile, a row and the 32-wide k block; lane group g reads elements
+// [32kb + 8g, 32kb + 8g + 8) of the row (both operands agree on that order).
+// ---------------------------------------------------------------------------
+template <bool F32C> struct Arith;
+
+template <> struct Arith<false> {  // bf16 operands, fp32 accumulate
+  using E = bf16_t;
+  struct BReg { bf16x8 v; };
+  static __device__ __forceinline__ E cvt(float x) { return f32_to_bf16(x); }
+  static __device__ __forceinline__ float tof(E x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ BReg breg(floatx4 t0, floatx4 t1) {
+    BReg b;
+    b.v = to_bf16x8(floatx8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]});
+    return b;
+  }
+  template <int COLS>
+  static __device__ __forceinline__ floatx4 k32(floatx4 acc, const E *tile, int row, int kb, int g,
+                                               const BReg &b) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    return mfma_bf16_k32(a, b.v, acc);
+  }
+  // acc += A . B with the A operand in registers and B read from an LDS row
+  template <int COLS>
+  static __device__ __forceinline__ floatx4 k32_regA(floatx4 acc, const BReg &a, const E *tile, int row,
+                                                    int kb, int g) {
+    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    return mfma_bf16_k32(a.v, b, acc);
+  }
+  template <int COLS>
+  static __device__ __forceinline__ BReg breg_lds(const E *tile, int row, int kb, int g) {
+    BReg b;
+    b.v = *reinterpret_cast<const bf16x8 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    return b;
+  }
+  // B operand from LDS scaled per k (sc points at the natural-order scale row)
+  template <int COLS>
+  static __device__ __forceinline__ BReg breg_lds_scaled(const E *tile, int row, int kb, int g,
+                                                         const float *sc) {
+    const bf16x8 raw = *reinterpret_cast<const bf16x8 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    const float4 s0 = *reinterpret_cast<const float4 *>(sc + 32 * kb + 8 * g);
+    const float4 s1 = *reinterpret_cast<const float4 *>(sc + 32 * kb + 8 * g + 4);
+    const floatx8 f = __builtin_convertvector(raw, floatx8) *
+                      floatx8{s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    BReg b;
+    b.v = to_bf16x8(f);
+    return b;
+  }
+  // 16x16x16 step: acc += A . B with A given row-wise (4 values of row j, k = 4g..4g+3)
+  // and B in accumulator layout (4 values: rows 4g..4g+3 of column j).
+  static __device__ __forceinline__ floatx4 k16(floatx4 acc, floatx4 a, floatx4 b) {
+    return mfma_bf16_k16(to_bf16x4(a), to_bf16x4(b), acc);
+  }
+  static __device__ __forceinline__ void store4(E *p, const float *x) {  // 4 consecutive
+    *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(floatx4{x[0], x[1], x[2], x[3]});
+  }
+  static __device__ __forceinline__ floatx4 load4(const E *p) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(p);
+    return floatx4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+};
+
+template <> struct Arith<true> {  // fp32 operands, fp32 MFMA
+  using E = float;
+  struct BReg { float v[8]; };
+  static __device__ __forceinline__ E cvt(float x) { return x; }
+  static __device__ __forceinline__ float tof(E x) { return x; }
+  static __device__ __forceinline__ BReg breg(floatx4 t0, floatx4 t1) {
+    BReg b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b.v[e] = t0[e];
+      b.v[4 + e] = t1[e];
+    }
+    return b;
+  }
+  template <int COLS>
+  static __device__ __forceinline__ floatx4 k32(floatx4 acc, const E *tile, int row, int kb, int g,
+                                               const BReg &b) {
+    const float4 a0 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    const float4 a1 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g + 4));
+    const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(a[e], b.v[e], acc);
+    return acc;
+  }
+  template <int COLS>
+  static __device__ __forceinline__ floatx4 k32_regA(floatx4 acc, const BReg &a, const E *tile, int row,
+                                                    int kb, int g) {
+    const float4 b0 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    const float4 b1 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g + 4));
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(a.v[e], bv[e], acc);
+    return acc;
+  }
+  template <int COLS>
+  static __device__ __forceinline__ BReg breg_lds(const E *tile, int row, int kb, int g) {
+    const float4 b0 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g));
+    const float4 b1 = *reinterpret_cast<const float4 *>(tile + Tile<E, COLS>::idx(row, 32 * kb + 8 * g + 4));
+    BReg b = {{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w}};
+    return b;
+  }
+  template <int COLS>
+  static __device__ __forceinline__ BReg breg_lds_scaled(const E *tile, int row, int kb, int g,
+                                                         const float *sc) {
+    BReg b = breg_lds<COLS>(tile, row, kb, g);
+    const float4 s0 = *reinterpret_cast<const float4 *>(sc + 32 * kb + 8 * g);
+    const float4 s1 = *reinterpret_cast<const float4 *>(sc + 32 * kb + 8 * g + 4);
+    b.v[0] *= s0.x; b.v[1] *= s0.y; b.v[2] *= s0.z; b.v[3] *= s0.w;
+    b.v[4] *= s1.x; b.v[5] *= s1.y; b.v[6] *= s1.z; b.v[7] *= s1.w;
+    return b;
+  }
+  static __device__ __forceinline__ floatx4 k16(floatx4 acc, floatx4 a, floatx4 b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(a[e], b[e], acc);
+    return acc;
+  }
+  static __device__ __forceinline__ void store4(E *p, const float *x) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+  static __device__ __forceinline__ floatx4 load4(const E *p) {
+    const float4 w = *reinterpret_cast<const float4 *>(p);
+    return floatx4{w.x, w.y, w.z, w.w};
+  }
+};
+
+// ---- document and chunk bookkeeping ----------------------------------------
+// document offsets; cu == nullptr means one document [0, T)
+__device__ __forceinline__ int64_t cu_at(const int32_t *cu, int64_t T, int i) {
+  return cu ? (int64_t)cu[i] : (i == 0 ? (int64_t)0 : T);
+}
+// largest d in [0, N-1] with cu[d] <= pos (skips empty documents starting at pos)
+__device__ __forceinline__ int doc_of(const int32_t *cu, int N, int64_t pos) {
+  if (!cu) return 0;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  return uni(lo);
+}
+// document owning a chunk slot (first_slot in kda_launch.h): largest d with first_slot(d) <= slot
+__device__ __forceinline__ int doc_of_slot(const int32_t *cu, int N, int64_t slot) {
+  if (!cu) return 0;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first_slot(cu[mid], mid) <= slot) lo = mid; else hi = mid - 1;
+  }
+  return uni(lo);
+}
+
+// ---- LDS shared by the prep stages -------------------------------------------
+struct PrepLds {
+  float GC2[D];       // G_C (base 2)
+  float Gref[4][D];   // G (base 2) at the first token of each subtile
+  float F[6][D];      // e^(Gref[I] - Gref[J]) for I > J
+  float beta[CH];
+  float wtot[4][D];   // per-wave cumulative-sum totals
+};
+
+// a1: gate and inclusive cumulative sum over the chunk (base 2).  Tokens at or
+// beyond len are padding: no decay.  Leaves G[r][c] for this thread's tokens
+// and channels, beta, Gref and GC2 in LDS; ends with a barrier.
+template <class IO>
+__device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO::raw8 (&Rz)[4],
+                                                 typename IO::raw1 Rb, float c1, float gmin2,
+                                                 int len, int tid, int w, int tq, int cg,
+                                                 float (&G)[4][8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float gm = (16 * w + 4 * tq + r < len) ? gmin2 : 0.f;
+    float zz[8];
+    IO::cvt8(Rz[r], zz);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) G[r][c] = kda_gate2(zz[c], c1, gm);
+  }
+  if (tid < CH) ps.beta[tid] = IO::cvt1(Rb);
+  // in-lane over r, across the 4 token groups of the wave (lanes 16 apart),
+  // then across waves
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    G[1][c] += G[0][c];
+    G[2][c] += G[1][c];
+    G[3][c] += G[2][c];
+    const float tot = G[3][c];
+    const float up16 = __shfl_up(tot, 16);
+    const float x1 = tot + (tq >= 1 ? up16 : 0.f);
+    const float up32 = __shfl_up(x1, 32);
+    const float excl = x1 + (tq >= 2 ? up32 : 0.f) - tot;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) G[r][c] += excl;
+  }
+  if (tq == 3) {
+    *reinterpret_cast<float4 *>(&ps.wtot[w][8 * cg]) = make_float4(G[3][0], G[3][1], G[3][2], G[3][3]);
+    *reinterpret_cast<float4 *>(&ps.wtot[w][8 * cg + 4]) = make_float4(G[3][4], G[3][5], G[3][6], G[3][7]);
+  }
+  __syncthreads();
+  SCHED_FENCE();
+  {
+    const float4 t0a = *reinterpret_cast<const float4 *>(&ps.wtot[0][8 * cg]);
+    const float4 t0b = *reinterpret_cast<const float4 *>(&ps.wtot[0][8 * cg + 4]);
+    const float4 t1a = *reinterpret_cast<const float4 *>(&ps.wtot[1][8 * cg]);
+    const float4 t1b = *reinterpret_cast<const float4 *>(&ps.wtot[1][8 * cg + 4]);
+    const float4 t2a = *reinterpret_cast<const float4 *>(&ps.wtot[2][8 * cg]);
+    const float4 t2b = *reinterpret_cast<const float4 *>(&ps.wtot[2][8 * cg + 4]);
+    const float t0[8] = {t0a.x, t0a.y, t0a.z, t0a.w, t0b.x, t0b.y, t0b.z, t0b.w};
+    const float t1[8] = {t1a.x, t1a.y, t1a.z, t1a.w, t1b.x, t1b.y, t1b.z, t1b.w};
+    const float t2[8] = {t2a.x, t2a.y, t2a.z, t2a.w, t2b.x, t2b.y, t2b.z, t2b.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float off = (w > 0 ? t0[c] : 0.f) + (w > 1 ? t1[c] : 0.f) + (w > 2 ? t2[c] : 0.f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) G[r][c] += off;
+    }
+  }
+  if (tq == 0) {
+    *reinterpret_cast<float4 *>(&ps.Gref[w][8 * cg]) = make_float4(G[0][0], G[0][1], G[0][2], G[0][3]);
+    *reinterpret_cast<float4 *>(&ps.Gref[w][8 * cg + 4]) = make_float4(G[0][4], G[0][5], G[0][6], G[0][7]);
+  }
+  if (w == 3 && tq == 3) {
+    *reinterpret_cast<float4 *>(&ps.GC2[8 * cg]) = make_float4(G[3][0], G[3][1], G[3][2], G[3][3]);
+    *reinterpret_cast<float4 *>(&ps.GC2[8 * cg + 4]) = make_float4(G[3][4], G[3][5], G[3][6], G[3][7]);
+  }
+  __syncthreads();
+  SCHED_FENCE();
+}
+
+// a2: decay factors of this thread's 4 tokens x 8 channels.  The subtile
+// operands Qh, Kh, Ki go to LDS tiles (natural channel order); per token row
+// i the sink receives K_decay and Q_decay (row_sink(i, kdec[8], qdec[8]));
+// K_restore is returned for the caller to store.
+template <class Ar, class IO, class RowSink>
+__device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename Ar::E *Qh,
+                                                    typename Ar::E *Kh, typename Ar::E *Ki,
+                                                    const typename IO::raw8 (&Rq)[4],
+                                                    const typename IO::raw8 (&Rk)[4],
+                                                    const float (&G)[4][8], int w, int tq, int cg,
+                                                    float (&Kres)[4][8], RowSink &&row_sink) {
+  using TD = Tile<typename Ar::E, D>;
+  float Pj[8], Rj[8], gref[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    gref[c] = ps.Gref[w][8 * cg + c];
+    Pj[c] = __builtin_amdgcn_exp2f(gref[c]);                       // e^(G_s)
+    Rj[c] = __builtin_amdgcn_exp2f(ps.GC2[8 * cg + c] - gref[c]);  // e^(G_C - G_s) <= 1
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * w + 4 * tq + r;
+    float qv[8], kv[8], qh[8], kh[8], ki[8], qdec[8], kdec[8];
+    IO::cvt8(Rq[r], qv);
+    IO::cvt8(Rk[r], kv);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float e1 = __builtin_amdgcn_exp2f(G[r][c] - gref[c]);  // <= 1
+      const float e2 = __builtin_amdgcn_rcpf(e1);                   // < e^75
+      qh[c] = qv[c] * e1;
+      kh[c] = kv[c] * e1;
+      ki[c] = kv[c] * e2;
+      qdec[c] = qh[c] * Pj[c];
+      kdec[c] = kh[c] * Pj[c];
+      Kres[r][c] = ki[c] * Rj[c];
+    }
+    Ar::store4(&Qh[TD::idx(i, 8 * cg)], qh);
+    Ar::store4(&Qh[TD::idx(i, 8 * cg + 4)], qh + 4);
+    Ar::store4(&Kh[TD::idx(i, 8 * cg)], kh);
+    Ar::store4(&Kh[TD::idx(i, 8 * cg + 4)], kh + 4);
+    Ar::store4(&Ki[TD::idx(i, 8 * cg)], ki);
+    Ar::store4(&Ki[TD::idx(i, 8 * cg + 4)], ki + 4);
+    row_sink(i, kdec, qdec);
+    SCHED_FENCE();
+  }
+}
+
+// F[pair][c] = e^(Gref[I][c] - Gref[J][c]), pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+__device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
+  for (int x = tid; x < 6 * D; x += FWD_THREADS) {
+    const int pi = x / D, c = x % D;
+    const int I = (pi == 0) ? 1 : (pi < 3 ? 2 : 3);
+    const int J = (pi == 0) ? 0 : (pi < 3 ? pi - 1 : pi - 3);
+    ps.F[pi][c] = __builtin_amdgcn_exp2f(ps.Gref[I][c] - ps.Gref[J][c]);
+  }
+}
+
+// a3: A_qk and A_kk per subtile pair (I >= J); wave w takes pairs w, w+4, w+8.
+// Products are formed transposed, (K_inv_J)(Q_I)^T, so lane (g, j) ends up
+// with row j of the pair's tile at columns 4g..4g+3 and writes them at once.
+// L (fp32, natural order) goes to LDS; M_qk goes to mqk_sink(row, J, mq[4]).
+template <class Ar, class MqkSink>
+__device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const typename Ar::E *Qh,
+                                                      const typename Ar::E *Kh,
+                                                      const typename Ar::E *Ki, float *L, int w,
+                                                      int g, int j, MqkSink &&mqk_sink) {
+  using BReg = typename Ar::BReg;
+  using TL = Tile<float, CH>;
+  for (int pidx = w; pidx < 10; pidx += 4) {
+    const int I = (pidx == 0) ? 0 : (pidx < 3 ? 1 : (pidx < 6 ? 2 : 3));
+    const int J = pidx - I * (I + 1) / 2;
+    floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      BReg kin;  // key side of subtile J, referenced to the first token of subtile I
+      if (I == J) {
+        kin = Ar::template breg_lds<D>(Ki, 16 * J + j, kb, g);
+      } else {
+        const int fp = I * (I - 1) / 2 + J;
+        kin = Ar::template breg_lds_scaled<D>(Ki, 16 * J + j, kb, g, ps.F[fp]);
+      }
+      aq = Ar::template k32_regA<D>(aq, kin, Qh, 16 * I + j, kb, g);
+      ak = Ar::template k32_regA<D>(ak, kin, Kh, 16 * I + j, kb, g);
+    }
+    // lane (g, j): element r is (row j of subtile I, column 4g + r of subtile J)
+    const int row = 16 * I + j;
+    const float bi = ps.beta[row];
+    float mq[4], lk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = 4 * g + r;
+      mq[r] = (I > J || col <= j) ? aq[r] : 0.f;        // diagonal kept
+      lk[r] = (I > J || col < j) ? bi * ak[r] : 0.f;    // strictly lower
+    }
+    mqk_sink(row, J, mq);
+    *reinterpret_cast<float4 *>(&L[TL::idx(row, 16 * J + 4 * g)]) = make_float4(lk[0], lk[1], lk[2], lk[3]);
+  }
+}
+
+// 16x16 tiles in accumulator layout: element r of lane (g, j) is (4g + r, j).
+__device__ __forceinline__ floatx4 add_identity(floatx4 x, int g, int j, float s) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] += (4 * g + r == j) ? s : 0.f;
+  return x;
+}
+
+// Inverse of a 16x16 unit lower-triangular I + L with nilpotent L (L^16 = 0):
+//   (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8).
+// A 16x16x16 MFMA takes its A operand row-wise, which is the accumulator layout
+// of the transpose, so every power is formed in both orientations:
+//   Lt is L^T in accumulator layout (= L in A layout), Ln is L itself.
+// Returns T = (I + L)^-1 in accumulator layout.
+template <class Ar>
+__device__ __forceinline__ floatx4 unit_lower_inverse(floatx4 Ln, floatx4 Lt, int g, int j) {
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  floatx4 L2 = Ar::k16(z, Lt, Ln);   // L L        (A = L, B = L)
+  floatx4 L2t = Ar::k16(z, Ln, Lt);  // L^T L^T    (A = L^T, B = L^T)
+  floatx4 L4 = Ar::k16(z, L2t, L2);
+  floatx4 L4t = Ar::k16(z, L2, L2t);
+  floatx4 L8t = Ar::k16(z, L4, L4t);
+  // R = (I + L^8)(I + L^4)(I + L^2)(I - L), right to left; the factors commute
+  floatx4 R = add_identity(-Ln, g, j, 1.f);
+  R = R + Ar::k16(z, L2t, R);  // (I + L^2) R
+  R = R + Ar::k16(z, L4t, R);  // (I + L^4) R
+  R = R + Ar::k16(z, L8t, R);  // (I + L^8) R
+  return R;
+}
+
+// a4 (i): inverse of the diagonal block w of I + L, stored to Tdg[w] (row-major)
+// and returned in accumulator layout.
+template <class Ar>
+__device__ __forceinline__ floatx4 prep_diag_inverse(const float *L, typename Ar::E (*Tdg)[SUB * SUB],
+                                                     int w, int g, int j) {
+  using TL = Tile<float, CH>;
+  floatx4 Ln, Lt;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Ln[r] = L[TL::idx(16 * w + 4 * g + r, 16 * w + j)];  // L (rows 4g+r, col j)
+    Lt[r] = L[TL::idx(16 * w + j, 16 * w + 4 * g + r)];  // L^T
+  }
+  const floatx4 T = unit_lower_inverse<Ar>(Ln, Lt, g, j);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Tdg[w][(4 * g + r) * SUB + j] = Ar::cvt(T[r]);
+  return T;
+}
+
+// Block column J of INV = (I + L)^-1 from the diagonal-block inverses T_II:
+//   X_JJ = T_JJ,  X_IJ = -T_II sum_{K=J}^{I-1} L_IK X_KJ  (I > J),
+// all tiles in registers (accumulator layout doubles as the 16x16x16 B operand).
+// Stores INV Diag(beta) into the 64x64 tile INVb with the token axis permuted.
+template <class Ar, int J>
+__device__ __forceinline__ void inv_block_column(const float *L, const typename Ar::E (*Tdg)[SUB * SUB],
+                                                 const float *beta, typename Ar::E *INVb,
+                                                 floatx4 Tjj, int g, int j) {
+  using TC = Tile<typename Ar::E, CH>;
+  using TL = Tile<float, CH>;
+  floatx4 X[4];
+  X[J] = Tjj;
+#pragma unroll
+  for (int I = J + 1; I < 4; ++I) {
+    floatx4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = J; K < I; ++K) {
+      const float4 l4 = *reinterpret_cast<const float4 *>(&L[TL::idx(16 * I + j, 16 * K + 4 * g)]);
+      R = Ar::k16(R, floatx4{l4.x, l4.y, l4.z, l4.w}, X[K]);
+    }
+    const floatx4 t = Ar::load4(&Tdg[I][j * SUB + 4 * g]);  // row j of T_II
+    floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+    Y = Ar::k16(Y, t, R);
+    X[I] = -Y;
+  }
+  const float bj = beta[16 * J + j];
+#pragma unroll
+  for (int I = J; I < 4; ++I) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      INVb[TC::idx(16 * I + 4 * g + r, kperm(16 * J + j))] = Ar::cvt(X[I][r] * bj);
+  }
+}
+
+// a4 (ii): wave w completes block column w (runtime wave index -> template).
+template <class Ar>
+__device__ __forceinline__ void prep_block_columns(const float *L,
+                                                   const typename Ar::E (*Tdg)[SUB * SUB],
+                                                   const float *beta, typename Ar::E *INVb,
+                                                   floatx4 Tww, int w, int g, int j) {
+  switch (w) {
+    case 0: inv_block_column<Ar, 0>(L, Tdg, beta, INVb, Tww, g, j); break;
+    case 1: inv_block_column<Ar, 1>(L, Tdg, beta, INVb, Tww, g, j); break;
+    case 2: inv_block_column<Ar, 2>(L, Tdg, beta, INVb, Tww, g, j); break;
+    default: inv_block_column<Ar, 3>(L, Tdg, beta, INVb, Tww, g, j); break;
+  }
+}
+
+// a5: one chunk of the recurrence for this wave's 16 state columns,
+//   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
+//   S <- Diag(gamma^C) S + K_restore^T U,
+// with S in fp32 MFMA accumulators (S[m] holds rows 16m + 4g + r, column j of
+// the slice) and V in accumulator layout (Vt[m]: tokens 16m + 4g + r).  The
+// operand tiles are the permuted-k LDS tiles the prep stages produce.  O rows
+// go through the bounded descriptor ro (tokens past the chunk are dropped) at
+// byte offset off_v + token * rowb; write_o = false skips O.
+template <class Ar, class IO>
+__device__ __forceinline__ void chunk_recurrence(const typename Ar::E *Kd, const typename Ar::E *Qd,
+                                                 const typename Ar::E *KrT, const typename Ar::E *Mqk,
+                                                 const typename Ar::E *INVb, const float *gamC,
+                                                 floatx4 (&S)[8], const floatx4 (&Vt)[4],
+                                                 bool write_o, __amdgpu_buffer_rsrc_t ro, int off_v,
+                                                 int rowb, int g, int j) {
+  using BReg = typename Ar::BReg;
+  BReg sb[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) sb[kb] = Ar::breg(S[2 * kb], S[2 * kb + 1]);
+
+  floatx4 U[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) x = Ar::template k32<D>(x, Kd, 16 * m + j, kb, g, sb[kb]);
+    U[m] = Vt[m] - x;  // V - K_decay S (Diag(beta) is folded into INV)
+  }
+  SCHED_FENCE();
+  BReg bb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) bb[kb] = Ar::breg(U[2 * kb], U[2 * kb + 1]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb <= (m >> 1); ++kb) x = Ar::template k32<CH>(x, INVb, 16 * m + j, kb, g, bb[kb]);
+    U[m] = x;
+  }
+  SCHED_FENCE();
+  BReg ub[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) ub[kb] = Ar::breg(U[2 * kb], U[2 * kb + 1]);
+
+  // O = Q_decay S + M_qk U  (off the serial state path)
+  if (write_o) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) x = Ar::template k32<D>(x, Qd, 16 * m + j, kb, g, sb[kb]);
+#pragma unroll
+      for (int kb = 0; kb <= (m >> 1); ++kb) x = Ar::template k32<CH>(x, Mqk, 16 * m + j, kb, g, ub[kb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) IO::st1(ro, x[r], off_v + (16 * m + r) * rowb);
+    }
+  }
+  SCHED_FENCE();
+  // S <- Diag(gamma^C) S + K_restore^T U
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float4 gc = *reinterpret_cast<const float4 *>(&gamC[16 * m + 4 * g]);
+    floatx4 x = S[m];
+    x[0] *= gc.x; x[1] *= gc.y; x[2] *= gc.z; x[3] *= gc.w;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) x = Ar::template k32<CH>(x, KrT, 16 * m + j, kb, g, ub[kb]);
+    S[m] = x;
+  }
+  SCHED_FENCE();
+}
+
+}  // namespace kda

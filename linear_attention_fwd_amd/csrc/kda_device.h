@@ -161,6 +161,29 @@ __device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, float x, in
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
 }
 
+// Global -> LDS copies that bypass registers.  A buffer load with the lds bit
+// writes 16 bytes per lane at M0 + 16 * lane (M0 = the wave-uniform LDS byte
+// address of the 1 KB block).  It is issued through inline asm: the compiler
+// otherwise makes every later LDS read wait for all such copies in flight,
+// including reads of a different buffer, which would serialise the double
+// buffering.  The caller waits (wait_vmem) and synchronises before reading
+// the copied data.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)uniptr(base);
+  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), uni(bytes), 0x00020000};
+}
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds_addr, int voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+// LDS byte address of a __shared__ object
+template <typename T> __device__ __forceinline__ uint32_t lds_addr(T *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)(p);
+}
+// s_waitcnt vmcnt(0): all vector memory operations of this wave have completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct bufio;
 template <> struct bufio<float> {
@@ -206,32 +229,26 @@ template <> struct bufio<bf16_t> {
   }
 };
 
-// A 128-row state slice in accumulator layout: tile[m][n][r] is row 16m + 4g + r,
-// column col0 + 16n + j of a row-major fp32 matrix with `ld` columns at `base`
+// A 128 x 16 state slice in accumulator layout: S[m][r] is row 16m + 4g + r,
+// column col0 + j of a row-major fp32 matrix with `ld` columns at `base`
 // (a wave-uniform pointer).
-template <int NT>
-__device__ __forceinline__ void state_load(floatx4 (&S)[8][NT], const float *base, int ld,
-                                           int col0, int g, int j) {
+__device__ __forceinline__ void state_load(floatx4 (&S)[8], const float *base, int ld, int col0,
+                                           int g, int j) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, D * ld * 4);
   const int voff = (4 * g * ld + col0 + j) * 4;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][n][e] = buf_ld_f32(r, voff + ((16 * m + e) * ld + 16 * n) * 4);
+    for (int e = 0; e < 4; ++e) S[m][e] = buf_ld_f32(r, voff + (16 * m + e) * ld * 4);
 }
-template <int NT>
-__device__ __forceinline__ void state_store(const floatx4 (&S)[8][NT], float *base, int ld,
-                                            int col0, int g, int j) {
+__device__ __forceinline__ void state_store(const floatx4 (&S)[8], float *base, int ld, int col0,
+                                            int g, int j) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, D * ld * 4);
   const int voff = (4 * g * ld + col0 + j) * 4;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) buf_st_f32(r, S[m][n][e], voff + ((16 * m + e) * ld + 16 * n) * 4);
+    for (int e = 0; e < 4; ++e) buf_st_f32(r, S[m][e], voff + (16 * m + e) * ld * 4);
 }
 
 // ---- XOR-swizzled LDS tiles -------------------------------------------------

@@ -29,6 +29,37 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd(FwdParams p, bool bf16_in, bool f32_compute, hipStream_t stream);
+
+// Chunk slots: chunk k of document d (chunks of 64 tokens restart at every
+// document start) lives in slot  first_slot(cu[d], d) + k  with
+// first_slot = floor(cu[d] / 64) + d.  The map is injective and needs no prefix
+// sum over documents; every slot lies in [0, n_chunk_slots(T, N)), and slots no
+// chunk maps to are skipped.
+__host__ __device__ inline int64_t first_slot(int64_t cu_d, int d) { return cu_d / 64 + d; }
+__host__ __device__ inline int64_t n_chunk_slots(int64_t T, int N) { return T / 64 + N; }
+
+// Two-kernel prefill over documents (bf16 inputs, bf16 MFMA operands): a
+// token-parallel prep kernel writes every (head, chunk) "chunk image" (the
+// recurrence operands, laid out as the recurrence kernel's LDS tiles) into the
+// workspace, then the recurrence kernel streams the images of each document
+// through double-buffered LDS.
+struct SplitParams {
+  const void *q, *k, *v, *z, *beta;
+  const float *A_log;
+  float g_min;
+  const int32_t *cu;       // [N+1] device document offsets, or nullptr = one document [0, T)
+  int N;
+  int64_t T;
+  int H;
+  const float *init;       // [N, H, D, D] initial states or nullptr (= 0)
+  void *o;                 // [T, H, D]
+  float *final_state;      // [N, H, D, D] or nullptr
+  void *ws;                // chunk images [H, n_slots, image]
+  int64_t n_slots;         // chunk slots per head (see first_slot)
+};
+size_t split_workspace_bytes(int64_t T, int N, int H);
+hipError_t launch_split(const SplitParams &p, hipStream_t stream);
+
 // final_state[d] = initial_state[d] (or 0) for every empty document d;
 // cu == nullptr means one document of T tokens.
 hipError_t launch_copy_empty(const int32_t *cu, int64_t T, const float *init, float *fin, int N,

@@ -79,12 +79,15 @@ def gpu_inputs(inp, device="cuda"):
     return t
 
 
-def gpu_chunk_fwd(inp, compute=0, t=None):
+def gpu_chunk_fwd(inp, compute=0, t=None, fused=False):
+    """kda_chunk_fwd on the GPU; fused=True runs the single-kernel path (no
+    workspace), otherwise the binding's default (two kernels for bf16 inputs)."""
     import linear_attention_fwd_amd as kda
     import torch
     t = t or gpu_inputs(inp)
     o, S = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min,
-                             t["S0"], t["cu"], t["cu_host"], compute=compute)
+                             t["S0"], t["cu"], t["cu_host"], compute=compute,
+                             workspace=False if fused else None)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 

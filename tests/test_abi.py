@@ -69,7 +69,7 @@ def _prefill(lib, fn="kda_chunk_fwd", **kw):
     args = [a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["g_min"], a["S0"], a["cu"],
             a["cu_host"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"], a["compute"]]
     if fn == "kda_chunk_fwd":
-        return lib.kda_chunk_fwd(*args, a["o"], a["fin"], None)
+        return lib.kda_chunk_fwd(*args, a["o"], a["fin"], a["ws"], a["ws_bytes"], None)
     return lib.kda_segment_scan(*args, a["nseg"], a["o"], a["fin"], a["ws"], a["ws_bytes"], None)
 
 
@@ -109,6 +109,18 @@ def test_segment_scan_workspace_checks(lib):
         == KDA_ERR_WORKSPACE
     assert _prefill(lib, "kda_segment_scan", nseg=4, S0=FAKE, fin=FAKE, ws=FAKE,
                     ws_bytes=need) == KDA_ERR_UNSUPPORTED
+
+
+def test_chunk_fwd_workspace_checks(lib):
+    # one 65 KiB chunk image per head and slot, floor(T / 64) + N slots per head
+    need = lib.kda_chunk_fwd_workspace_size(1, 128, 4, 128, 128)
+    assert need == (128 // 64 + 1) * 4 * 66560
+    assert lib.kda_chunk_fwd_workspace_size(3, 1000, 2, 128, 128) == (1000 // 64 + 3) * 2 * 66560
+    assert lib.kda_chunk_fwd_workspace_size(0, 128, 4, 128, 128) == 0
+    assert lib.kda_chunk_fwd_workspace_size(1, 128, 4, 64, 128) == 0
+    # the two-kernel path (bf16, compute AUTO) refuses a short or misaligned workspace
+    assert _prefill(lib, ws=FAKE, ws_bytes=need - 1) == KDA_ERR_WORKSPACE
+    assert _prefill(lib, ws=ctypes.c_void_p(0x1004), ws_bytes=need) == KDA_ERR_WORKSPACE
 
 
 def test_decode_validation(lib):

@@ -62,10 +62,28 @@ def test_chunk_fwd_matches_oracle(name):
     seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
     inp = kda_gen.make_prefill(seed, T, H, **kw)
     ref = oracle_forward(inp)
-    for compute in ((0,) if inp.dtype == "f32" else (0, 1)):
+    # bf16 inputs: the two-kernel path (workspace), the fused kernel, fp32 arithmetic
+    runs = ((0, False),) if inp.dtype == "f32" else ((0, False), (0, True), (1, False))
+    for compute, fused in runs:
         _case(inp, compute)
-        o, S = gpu_chunk_fwd(inp, compute=compute)
+        print(f"    path={'fused' if fused or inp.dtype == 'f32' or compute else 'prep+recurrence'}",
+              flush=True)
+        o, S = gpu_chunk_fwd(inp, compute=compute, fused=fused)
         _check_prefill(inp, o, S, _tols(inp, compute), ref)
+
+
+def test_two_kernel_path_matches_fused_kernel():
+    """Both prefill paths run the same stage code; they agree to well below the
+    bf16 tolerance (with identical compiled arithmetic, bit for bit)."""
+    inp = kda_gen.make_prefill(33, 777, 3, "bf16", lengths=[64, 1, 0, 300, 412],
+                               s0_std=0.02, s0_docs="all")
+    o1, S1 = gpu_chunk_fwd(inp)
+    o2, S2 = gpu_chunk_fwd(inp, fused=True)
+    print(f"    identical O: {np.array_equal(o1, o2)}, identical S: {np.array_equal(S1, S2)}",
+          flush=True)
+    eo, _ = rel_l2_slices(o1, o2, inp.cu_seqlens)
+    es, _ = rel_l2_slices(S1, S2, axis_tokens=False)
+    assert eo <= 1e-3 and es <= 1e-3, (eo, es)
 
 
 def test_chunk_fwd_is_deterministic():
@@ -123,7 +141,7 @@ def test_segment_scan_matches_oracle(name, n_seg):
 def test_segment_scan_one_segment_equals_chunk_fwd():
     inp = kda_gen.make_prefill(44, 640, 2, "bf16", lengths=[200, 440], s0_std=0.02,
                                s0_docs="all")
-    o1, S1 = gpu_chunk_fwd(inp)
+    o1, S1 = gpu_chunk_fwd(inp, fused=True)
     o2, S2 = gpu_segment_scan(inp, n_segments=1)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 

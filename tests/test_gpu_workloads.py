@@ -39,7 +39,10 @@ def test_single_sequence_workload():
     t = gpu_inputs(inp)
     o_ref, S_ref = oracle_forward(inp, group=16)
     o, S = gpu_chunk_fwd(inp, t=t)
-    eo, es = _report("bf16", o, o_ref, S, S_ref, inp.cu_seqlens)
+    eo, es = _report("bf16, prep + recurrence kernels", o, o_ref, S, S_ref, inp.cu_seqlens)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    of, Sf = gpu_chunk_fwd(inp, t=t, fused=True)
+    eo, es = _report("bf16, fused kernel", of, o_ref, Sf, S_ref, inp.cu_seqlens)
     assert eo <= TOL_BF16 and es <= TOL_BF16
     o32, S32 = gpu_chunk_fwd(inp, compute=1, t=t)
     eo, es = _report("fp32 arithmetic", o32, o_ref, S32, S_ref, inp.cu_seqlens)
