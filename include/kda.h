@@ -110,6 +110,31 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
  * (floor(T / 64) + N) slots per head.  0 for invalid sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv);
 
+/* The two halves of kda_chunk_fwd's two-kernel path, callable on their own
+ * (bf16 inputs and arithmetic only; KDA_ERR_UNSUPPORTED otherwise).
+ *
+ * kda_chunk_prep: token-parallel chunk prep over every (head, chunk) -- gate and
+ * in-chunk cumulative decay, decay factors, intra-chunk products and the UT
+ * transform ("序列维度（下）", sections "UT 变换" and "数值问题"; SemiAnalysis page,
+ * "FlashKDA 算法") -- written as one 65 KiB chunk image per (head, chunk slot)
+ * into workspace (kda_chunk_fwd_workspace_size bytes, 256-byte aligned).
+ *
+ * kda_chunk_recurrence: the serial chunk recurrence of every (document, head)
+ * over the images kda_chunk_prep wrote for the same q, k, g_logits, beta,
+ * A_log, g_min and cu_seqlens; reads v and initial_state, writes o and
+ * final_state (which may alias initial_state).  The workspace must not be
+ * modified in between; both calls must be on the same stream (or ordered). */
+int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const void *beta,
+                   const float *A_log, float g_min, const int32_t *cu_seqlens,
+                   const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
+                   int32_t dv, int32_t dtype, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                         int32_t dk, int32_t dv, int32_t dtype, const void *workspace,
+                         size_t workspace_bytes, void *o, float *final_state, void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* kda_segment_scan -- intra-device context parallelism for long prefill.
  *

@@ -26,7 +26,8 @@ KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_segment_scan",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_prep",
+           "kda_chunk_recurrence", "kda_segment_scan",
            "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_status_string", "kda_last_error")
 
@@ -53,6 +54,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, i32, i64, i32, i32, i32, i32,
+                                   vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_prep.restype = ctypes.c_int
+    lib.kda_chunk_recurrence.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp,
+                                         ctypes.c_size_t, vp, vp, vp]
+    lib.kda_chunk_recurrence.restype = ctypes.c_int
     lib.kda_segment_scan.argtypes = prefill + [i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_segment_scan.restype = ctypes.c_int
     lib.kda_segment_scan_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -179,6 +186,46 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                            dk, dv, _dtype_code(q), int(compute), _ptr(o), _ptr(final_state),
                            ws_ptr, ws_bytes, _stream())
     _check(rc)
+    return o, final_state
+
+
+def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -5.0,
+                   cu_seqlens=None, cu_seqlens_host=None) -> None:
+    """First half of the two-kernel prefill: writes every (head, chunk) image into
+    ``workspace`` (uint8, kda_chunk_fwd_workspace_size bytes).  bf16 inputs only."""
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, q, g_logits, beta, A_log, None,
+                                                       cu_seqlens, cu_seqlens_host)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g_logits), _ptr(beta), _ptr(A_log),
+                              float(g_min), _ptr(cu_dev), host_ptr, N, T, H, dk, dv,
+                              _dtype_code(q), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream()))
+
+
+def kda_chunk_recurrence(v, workspace, initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                         output_final_state: bool = True, o=None, final_state=None):
+    """Second half of the two-kernel prefill: the chunk recurrence over the images
+    kda_chunk_prep wrote.  Returns (o, final_state)."""
+    torch = _torch()
+    lib = load_library()
+    _dev(v, "v")
+    T, H, dv = v.shape
+    dk = dv
+    cu_dev, cu_host, N = _seqlens(cu_seqlens, cu_seqlens_host, T, v.device)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", torch.float32)
+        if tuple(initial_state.shape) != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be [{N},{H},{dk},{dv}]")
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    _check(lib.kda_chunk_recurrence(_ptr(v), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
+                                    dk, dv, _dtype_code(v), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(o),
+                                    _ptr(final_state), _stream()))
     return o, final_state
 
 

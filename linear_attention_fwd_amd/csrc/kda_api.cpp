@@ -30,13 +30,9 @@ int hip_fail(hipError_t e, const char *what) {
 
 constexpr int kD = 128;
 
-// Shared validation of the prefill entry points.
-int check_prefill(const void *q, const void *k, const void *v, const void *g_logits,
-                  const void *beta, float g_min, const int32_t *cu_seqlens,
-                  const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
-                  int32_t dv, int32_t dtype, int32_t compute, const void *o) {
-  if (T > 0 && (!q || !k || !v || !g_logits || !beta || !o))
-    return fail(KDA_ERR_NULL, "q, k, v, g_logits, beta and o must be non-NULL when T > 0");
+// Sizes, dtype and document offsets shared by the prefill entry points.
+int check_layout(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N, int64_t T,
+                 int32_t H, int32_t dk, int32_t dv, int32_t dtype) {
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported (got %d, %d)", dk, dv);
   if (H <= 0) return fail(KDA_ERR_SHAPE, "H must be positive (got %d)", H);
   if (T < 0) return fail(KDA_ERR_SHAPE, "T must be >= 0");
@@ -44,10 +40,6 @@ int check_prefill(const void *q, const void *k, const void *v, const void *g_log
   if (T > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "T must fit int32 offsets");
   if ((int64_t)N * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "N * H too large");
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
-  if (compute != KDA_COMPUTE_AUTO && compute != KDA_COMPUTE_F32)
-    return fail(KDA_ERR_DTYPE, "unknown compute mode %d", compute);
-  if (!(g_min >= -5.0f && g_min < 0.0f))
-    return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
   if (cu_seqlens) {
     if (!cu_seqlens_host)
       return fail(KDA_ERR_SEQLENS, "cu_seqlens_host is required with cu_seqlens");
@@ -61,6 +53,52 @@ int check_prefill(const void *q, const void *k, const void *v, const void *g_log
     return fail(KDA_ERR_SEQLENS, "cu_seqlens is required when N > 1");
   }
   return KDA_OK;
+}
+
+int check_gate(float g_min) {
+  if (!(g_min >= -5.0f && g_min < 0.0f))
+    return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
+  return KDA_OK;
+}
+
+// Shared validation of the full prefill entry points.
+int check_prefill(const void *q, const void *k, const void *v, const void *g_logits,
+                  const void *beta, float g_min, const int32_t *cu_seqlens,
+                  const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
+                  int32_t dv, int32_t dtype, int32_t compute, const void *o) {
+  if (T > 0 && (!q || !k || !v || !g_logits || !beta || !o))
+    return fail(KDA_ERR_NULL, "q, k, v, g_logits, beta and o must be non-NULL when T > 0");
+  int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
+  if (rc != KDA_OK) return rc;
+  if (compute != KDA_COMPUTE_AUTO && compute != KDA_COMPUTE_F32)
+    return fail(KDA_ERR_DTYPE, "unknown compute mode %d", compute);
+  return check_gate(g_min);
+}
+
+// Workspace of the two-kernel path (chunk images).
+int check_image_workspace(const void *workspace, size_t workspace_bytes, int64_t T, int32_t N,
+                          int32_t H) {
+  if (T == 0) return KDA_OK;
+  const size_t need = kda::split_workspace_bytes(T, N, H);
+  if (!workspace || workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (kda::n_chunk_slots(T, N) * H > (int64_t)INT32_MAX)
+    return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
+  return KDA_OK;
+}
+
+kda::SplitParams split_params(const void *q, const void *k, const void *v, const void *g_logits,
+                              const void *beta, const float *A_log, float g_min,
+                              const float *initial_state, const int32_t *cu_seqlens, int32_t N,
+                              int64_t T, int32_t H, void *o, float *final_state, const void *ws) {
+  kda::SplitParams p{};
+  p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
+  p.A_log = A_log; p.g_min = g_min;
+  p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
+  p.init = initial_state; p.o = o; p.final_state = final_state;
+  p.ws = const_cast<void *>(ws); p.n_slots = kda::n_chunk_slots(T, N);
+  return p;
 }
 
 bool has_empty_doc(const int32_t *cu_host, int32_t N, int64_t T) {
@@ -106,23 +144,16 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
   if (rc != KDA_OK) return rc;
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   const bool split = workspace != nullptr && !f32c;
-  if (split && T > 0) {
-    const size_t need = kda::split_workspace_bytes(T, N, H);
-    if (workspace_bytes < need)
-      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
-    if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (kda::n_chunk_slots(T, N) * H > (int64_t)INT32_MAX)
-      return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
+  if (split) {
+    rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+    if (rc != KDA_OK) return rc;
   }
   hipStream_t st = (hipStream_t)stream;
   if (T > 0 && split) {
-    kda::SplitParams p{};
-    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
-    p.A_log = A_log; p.g_min = g_min;
-    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
-    p.init = initial_state; p.o = o; p.final_state = final_state;
-    p.ws = workspace; p.n_slots = kda::n_chunk_slots(T, N);
-    hipError_t e = kda::launch_split(p, st);
+    const kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
+                                            cu_seqlens, N, T, H, o, final_state, workspace);
+    hipError_t e = kda::launch_chunk_prep(p, st);
+    if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
   } else if (T > 0) {
     kda::FwdParams p{};
@@ -145,6 +176,50 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv) {
   if (N <= 0 || T < 0 || H <= 0 || dk != kD || dv != kD) return 0;
   return kda::split_workspace_bytes(T, N, H);
+}
+
+int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const void *beta,
+                   const float *A_log, float g_min, const int32_t *cu_seqlens,
+                   const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
+                   int32_t dv, int32_t dtype, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  if (T > 0 && (!q || !k || !g_logits || !beta))
+    return fail(KDA_ERR_NULL, "q, k, g_logits and beta must be non-NULL when T > 0");
+  int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
+  if (rc == KDA_OK) rc = check_gate(g_min);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prep takes bf16 inputs only");
+  rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+  if (rc != KDA_OK || T == 0) return rc;
+  const kda::SplitParams p = split_params(q, k, nullptr, g_logits, beta, A_log, g_min, nullptr,
+                                          cu_seqlens, N, T, H, nullptr, nullptr, workspace);
+  hipError_t e = kda::launch_chunk_prep(p, (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_chunk_prep launch");
+}
+
+int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                         int32_t dk, int32_t dv, int32_t dtype, const void *workspace,
+                         size_t workspace_bytes, void *o, float *final_state, void *stream) {
+  if (T > 0 && (!v || !o)) return fail(KDA_ERR_NULL, "v and o must be non-NULL when T > 0");
+  int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_recurrence takes bf16 inputs only");
+  rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+  if (rc != KDA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    const kda::SplitParams p = split_params(nullptr, nullptr, v, nullptr, nullptr, nullptr, -5.0f,
+                                            initial_state, cu_seqlens, N, T, H, o, final_state,
+                                            workspace);
+    hipError_t e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_recurrence launch");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_recurrence empty documents");
+  }
+  return KDA_OK;
 }
 
 int kda_default_segments(void) {

@@ -58,7 +58,8 @@ struct SplitParams {
   int64_t n_slots;         // chunk slots per head (see first_slot)
 };
 size_t split_workspace_bytes(int64_t T, int N, int H);
-hipError_t launch_split(const SplitParams &p, hipStream_t stream);
+hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);
+hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);
 
 // final_state[d] = initial_state[d] (or 0) for every empty document d;
 // cu == nullptr means one document of T tokens.

@@ -11,7 +11,7 @@
 // FlashKDA structure of the SemiAnalysis page, section "FlashKDA 算法").
 //
 // Chunks restart at every document start; chunk k of document d has slot
-// first_slot(d) + k (kda_chunk.h), the images of head h lie at
+// first_slot(d) + k (kda_launch.h), the images of head h lie at
 // ws + (h * n_slots + slot) * sizeof(ChunkImage).
 #include <stddef.h>
 
@@ -180,8 +180,123 @@ struct __align__(16) RecSmem {
   ChunkImage buf[2];
 };
 
+// MFMA A-operand fragments of one chunk for one wave, read from the chunk image
+// in LDS ahead of use.  None depends on the state, so the reads of the state
+// path (K_decay, INV, K_restore^T, gamma) are all in flight before the chunk's
+// first product and the chain then runs without waiting on LDS; the output
+// operands (Q_decay, M_qk) are read once the first products are issued, into
+// registers the K_decay fragments free.  Lane (g, j) holds row 16m + j,
+// k elements 32kb + 8g .. +7 of each tile (the k32 operand layout).
+struct StateFrags {
+  bf16x8 kd[4][4];   // K_decay   [m][kb]
+  bf16x8 inv[6];     // INV Diag(beta), blocks (m, kb <= m/2) in m-major order
+  bf16x8 krt[8][2];  // K_restore^T [m][kb]
+  float4 gam[8];     // gamma^C rows 16m + 4g .. +3
+};
+struct OutFrags {
+  bf16x8 qd[4][4];   // Q_decay   [m][kb]
+  bf16x8 mqk[6];     // M_qk, as inv
+};
+
+__device__ __forceinline__ bf16x8 frag(const bf16_t *tile, int idx) {
+  return *reinterpret_cast<const bf16x8 *>(tile + idx);
+}
+__device__ __forceinline__ void load_state_frags(StateFrags &f, const ChunkImage &im, int g, int j) {
+  using TD = Tile<bf16_t, D>;
+  using TC = Tile<bf16_t, CH>;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) f.kd[m][kb] = frag(im.Kd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+  int x = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) f.inv[x] = frag(im.INVb, TC::idx(16 * m + j, 32 * kb + 8 * g));
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) f.krt[m][kb] = frag(im.KrT, TC::idx(16 * m + j, 32 * kb + 8 * g));
+#pragma unroll
+  for (int m = 0; m < 8; ++m) f.gam[m] = *reinterpret_cast<const float4 *>(&im.gamC[16 * m + 4 * g]);
+}
+__device__ __forceinline__ void load_out_frags(OutFrags &f, const ChunkImage &im, int g, int j) {
+  using TD = Tile<bf16_t, D>;
+  using TC = Tile<bf16_t, CH>;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) f.qd[m][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+  int x = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) f.mqk[x] = frag(im.Mqk, TC::idx(16 * m + j, 32 * kb + 8 * g));
+}
+
+__device__ __forceinline__ bf16x8 pack_tiles(floatx4 t0, floatx4 t1) {
+  return to_bf16x8(floatx8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]});
+}
+
+// The chunk recurrence (chunk_recurrence in kda_chunk.h) on staged fragments:
+//   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
+//   S <- Diag(gamma^C) S + K_restore^T U.
+__device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], const floatx4 (&Vt)[4],
+                                         __amdgpu_buffer_rsrc_t ro, int off_v, int rowb, int g,
+                                         int j) {
+  using IO = bufio<bf16_t>;
+  StateFrags f;
+  load_state_frags(f, im, g, j);
+  bf16x8 sb[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) sb[kb] = pack_tiles(S[2 * kb], S[2 * kb + 1]);
+  floatx4 U[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(f.kd[m][kb], sb[kb], x);
+    U[m] = Vt[m] - x;
+  }
+  SCHED_FENCE();
+  OutFrags fo;
+  load_out_frags(fo, im, g, j);
+  bf16x8 bb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
+  int x = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(f.inv[x], bb[kb], acc);
+    U[m] = acc;
+  }
+  bf16x8 ub[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) ub[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    floatx4 acc = S[m];
+    acc[0] *= f.gam[m].x; acc[1] *= f.gam[m].y; acc[2] *= f.gam[m].z; acc[3] *= f.gam[m].w;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(f.krt[m][kb], ub[kb], acc);
+    S[m] = acc;
+  }
+  x = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(fo.qd[m][kb], sb[kb], acc);
+#pragma unroll
+    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(fo.mqk[x], ub[kb], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) IO::st1(ro, acc[r], off_v + (16 * m + r) * rowb);
+  }
+}
+
 __global__ void __launch_bounds__(FWD_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
-  using Ar = Arith<false>;
   using IO = bufio<bf16_t>;
   constexpr int ES = 2;
   __shared__ RecSmem sm;
@@ -255,11 +370,8 @@ __global__ void __launch_bounds__(FWD_THREADS, 1) kda_chunk_rec_kernel(SplitPara
       issue_image(kk + 1);
       fetch_v(kk + 1);
     }
-    SCHED_FENCE();
-    const ChunkImage &im = sm.buf[kk & 1];
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + (cs * H + h) * D, ((len - 1) * H + 1) * D * ES);
-    chunk_recurrence<Ar, IO>(im.Kd, im.Qd, im.KrT, im.Mqk, im.INVb, im.gamC, S, Vt, true, ro, off_v,
-                             rowb, g, j);
+    rec_step(sm.buf[kk & 1], S, Vt, ro, off_v, rowb, g, j);
   }
   if (p.final_state) state_store(S, uniptr(p.final_state + ((int64_t)d * H + h) * (D * D)), D, colW, g, j);
 }
@@ -268,11 +380,13 @@ size_t split_workspace_bytes(int64_t T, int N, int H) {
   return (size_t)n_chunk_slots(T, N) * (size_t)H * (size_t)IMG_BYTES;
 }
 
-hipError_t launch_split(const SplitParams &p, hipStream_t stream) {
-  const int64_t prep_blocks = p.n_slots * p.H;
-  hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3((unsigned)prep_blocks), dim3(FWD_THREADS), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
+  const int64_t blocks = p.n_slots * p.H;
+  hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3((unsigned)blocks), dim3(FWD_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
   const int units = p.N * p.H;
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * 2)), dim3(FWD_THREADS), 0, stream, p);

@@ -123,6 +123,38 @@ def test_chunk_fwd_workspace_checks(lib):
     assert _prefill(lib, ws=ctypes.c_void_p(0x1004), ws_bytes=need) == KDA_ERR_WORKSPACE
 
 
+def test_prep_and_recurrence_validation(lib):
+    need = lib.kda_chunk_fwd_workspace_size(1, 128, 4, 128, 128)
+
+    def prep(**kw):
+        a = dict(q=FAKE, g_min=-5.0, N=1, T=128, H=4, dk=128, dtype=1, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return lib.kda_chunk_prep(a["q"], FAKE, FAKE, FAKE, None, a["g_min"], None, None, a["N"],
+                                  a["T"], a["H"], a["dk"], 128, a["dtype"], a["ws"], a["ws_bytes"],
+                                  None)
+
+    def rec(**kw):
+        a = dict(v=FAKE, o=FAKE, N=1, T=128, H=4, dtype=1, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return lib.kda_chunk_recurrence(a["v"], None, None, None, a["N"], a["T"], a["H"], 128, 128,
+                                        a["dtype"], a["ws"], a["ws_bytes"], a["o"], None, None)
+
+    assert prep(q=None) == KDA_ERR_NULL
+    assert prep(dk=64) == KDA_ERR_SHAPE
+    assert prep(g_min=-6.0) == KDA_ERR_GATE_BOUND
+    assert prep(dtype=0) == KDA_ERR_UNSUPPORTED      # bf16 inputs only
+    assert prep(ws=None) == KDA_ERR_WORKSPACE
+    assert prep(ws_bytes=need - 1) == KDA_ERR_WORKSPACE
+    assert prep(N=2) == KDA_ERR_SEQLENS
+    assert prep(T=0) == KDA_OK                       # nothing to do, nothing launched
+    assert rec(v=None) == KDA_ERR_NULL
+    assert rec(o=None) == KDA_ERR_NULL
+    assert rec(H=0) == KDA_ERR_SHAPE
+    assert rec(dtype=0) == KDA_ERR_UNSUPPORTED
+    assert rec(ws=ctypes.c_void_p(0x1008)) == KDA_ERR_WORKSPACE
+    assert rec(ws_bytes=0) == KDA_ERR_WORKSPACE
+
+
 def test_decode_validation(lib):
     def call(**kw):
         a = dict(state=FAKE, slots=None, c=FAKE, acc=FAKE, W=4, n=FAKE, A=None, g_min=-5.0,

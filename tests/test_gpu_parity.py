@@ -86,6 +86,25 @@ def test_two_kernel_path_matches_fused_kernel():
     assert eo <= 1e-3 and es <= 1e-3, (eo, es)
 
 
+def test_prep_then_recurrence_equals_chunk_fwd():
+    """The two halves called on their own give kda_chunk_fwd's result exactly."""
+    import torch
+    import linear_attention_fwd_amd as kda
+    from kda_testlib import gpu_inputs
+    inp = kda_gen.make_prefill(34, 450, 3, "bf16", lengths=[200, 0, 250], s0_std=0.02,
+                               s0_docs="all")
+    t = gpu_inputs(inp)
+    o1, S1 = gpu_chunk_fwd(inp, t=t)
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_size(inp.N, inp.T, inp.H), dtype=torch.uint8,
+                     device="cuda")
+    kda.kda_chunk_prep(t["q"], t["k"], t["z"], t["beta"], ws, t["A_log"], inp.g_min, t["cu"],
+                       t["cu_host"])
+    o2, S2 = kda.kda_chunk_recurrence(t["v"], ws, t["S0"], t["cu"], t["cu_host"])
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, kda_gen.from_torch(o2))
+    assert np.array_equal(S1, kda_gen.from_torch(S2))
+
+
 def test_chunk_fwd_is_deterministic():
     inp = kda_gen.make_prefill(31, 500, 4, "bf16", s0_std=0.02, s0_docs="all")
     o1, S1 = gpu_chunk_fwd(inp)
