@@ -106,7 +106,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                   float *final_state, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kda_chunk_fwd's two-kernel path needs for N documents of T
- * tokens in total and H heads: one 65 KiB image per head and chunk slot,
+ * tokens in total and H heads: one 62 KiB image per head and chunk slot,
  * (floor(T / 64) + N) slots per head.  0 for invalid sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv);
 
@@ -116,7 +116,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk,
  * kda_chunk_prep: token-parallel chunk prep over every (head, chunk) -- gate and
  * in-chunk cumulative decay, decay factors, intra-chunk products and the UT
  * transform ("序列维度（下）", sections "UT 变换" and "数值问题"; SemiAnalysis page,
- * "FlashKDA 算法") -- written as one 65 KiB chunk image per (head, chunk slot)
+ * "FlashKDA 算法") -- written as one 62 KiB chunk image per (head, chunk slot)
  * into workspace (kda_chunk_fwd_workspace_size bytes, 256-byte aligned).
  *
  * kda_chunk_recurrence: the serial chunk recurrence of every (document, head)

@@ -168,21 +168,49 @@ __device__ __forceinline__ void buf_st_f32(__amdgpu_buffer_rsrc_t r, float x, in
 // including reads of a different buffer, which would serialise the double
 // buffering.  The caller waits (wait_vmem) and synchronises before reading
 // the copied data.
+//
+// The compiler does not insert the wait states the hardware needs in front of
+// an asm memory instruction: a vector memory read of an SGPR that a VALU
+// instruction (v_readfirstlane, which builds the descriptor) wrote needs 5,
+// and an LDS-DMA load after an SALU write of M0 needs 1.  Every asm load here
+// therefore starts with s_nop 4 (5 wait states).
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)uniptr(base);
   return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), uni(bytes), 0x00020000};
 }
+// No memory clobber: the target LDS buffer is not accessed by the compiler's
+// code until a later barrier (which has one), and volatile asm keeps its order
+// relative to the other asm statements here.
 __device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, uint32_t lds_addr, int voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
-               : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "{m0}"(lds_addr));
 }
 // LDS byte address of a __shared__ object
 template <typename T> __device__ __forceinline__ uint32_t lds_addr(T *p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)(p);
 }
+// One dword per lane from global memory into LDS (lane l -> lds_addr + 4 l).  Used
+// to pull lines into L2 ahead of a later copy: the data lands in a scratch LDS
+// area nobody reads.  Offsets past the descriptor's size fetch nothing.
+__device__ __forceinline__ void touch4_to_lds(i32x4 rsrc, uint32_t lds_addr, int voff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "{m0}"(lds_addr)
+               : "memory");
+}
 // s_waitcnt vmcnt(0): all vector memory operations of this wave have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recently issued vector memory
+// operations of this wave have completed (they complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vmem_except_last() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for this wave's outstanding global memory operations.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct bufio;

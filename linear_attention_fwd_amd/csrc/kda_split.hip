@@ -5,10 +5,12 @@
 // workgroup per chunk, two workgroups per compute unit.  It writes the
 // recurrence operands of its chunk, the "chunk image", to a workspace in the
 // exact layout of the recurrence kernel's LDS tiles.  The recurrence kernel
-// then runs the serial chain of each (document, head, 64-column slice) and only
-// streams images: global -> LDS copies into a double buffer, one chunk ahead
-// of the MFMA work (the split into a prep kernel and a recurrence kernel is the
-// FlashKDA structure of the SemiAnalysis page, section "FlashKDA 算法").
+// then runs the serial chain of each (document, head, 64-column slice) and
+// only streams images: global -> LDS copies into a double buffer, one chunk
+// ahead of the MFMA work and issued by waves of their own, with the lines of a
+// later chunk pulled into L2 before that (the split into a
+// prep kernel and a recurrence kernel is the FlashKDA structure of the
+// SemiAnalysis page, section "FlashKDA 算法").
 //
 // Chunks restart at every document start; chunk k of document d has slot
 // first_slot(d) + k (kda_launch.h), the images of head h lie at
@@ -19,15 +21,30 @@
 
 namespace kda {
 
+// M_qk and INV Diag(beta) as the recurrence reads them: its 32-wide k steps
+// over rows 0..31 stop at column 31, so the top-right 32 x 32 quarter is never
+// read and is not stored.  Rows 0..31 are 32 wide, rows 32..63 are 64 wide,
+// each part XOR-swizzled like Tile (token axis permuted, see kperm).
+struct PackedLower {
+  using Top = Tile<bf16_t, 32>;
+  using Bot = Tile<bf16_t, 64>;
+  static constexpr int TOP = 32 * 32;
+  static constexpr int ELEMS = TOP + 32 * 64;
+  // element offset of logical (r, col); col < 32 when r < 32
+  static __device__ __forceinline__ int idx(int r, int col) {
+    return r < 32 ? Top::idx(r, col) : TOP + Bot::idx(r - 32, col);
+  }
+};
+
 // Recurrence operands of one (head, chunk), laid out as LDS tiles.
 struct __align__(16) ChunkImage {
-  bf16_t Kd[CH * D];     // K_decay, channel axis permuted
-  bf16_t Qd[CH * D];     // Q_decay, channel axis permuted
-  bf16_t KrT[D * CH];    // K_restore^T, token axis permuted
-  bf16_t Mqk[CH * CH];   // M_qk, token axis permuted
-  bf16_t INVb[CH * CH];  // INV Diag(beta), token axis permuted
-  float gamC[D];         // gamma^C
-  float pad[D];          // the image is a whole number of 1 KB copy blocks
+  bf16_t Kd[CH * D];                 // K_decay, channel axis permuted
+  bf16_t Qd[CH * D];                 // Q_decay, channel axis permuted
+  bf16_t KrT[D * CH];                // K_restore^T, token axis permuted
+  bf16_t Mqk[PackedLower::ELEMS];    // M_qk
+  bf16_t INVb[PackedLower::ELEMS];   // INV Diag(beta)
+  float gamC[D];                     // gamma^C
+  float pad[384];                    // the image is a whole number of 1 KB copy blocks
 };
 constexpr int IMG_BYTES = (int)sizeof(ChunkImage);
 constexpr int IMG_BLOCKS = IMG_BYTES / 1024;
@@ -145,12 +162,12 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitPar
 
   prep_subtile_products<Ar>(sm.ps, sm.u.p1.Qh, sm.u.p1.Kh, sm.u.p1.Ki, sm.L, w, g, j,
                             [&](int row, int J, const float *mq) {
-                              img_st4(ri, OFF_MQK + 2 * TC::idx(row, kperm(16 * J + 4 * g)), mq);
+                              img_st4(ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(16 * J + 4 * g)), mq);
                             });
   // The recurrence reads the upper blocks (0,1) and (2,3) of M_qk and INV Diag(beta)
   // (its 32-wide k steps span two subtiles); they must hold zeros.
   const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-  if (w & 1) img_st4(ri, OFF_MQK + 2 * TC::idx(16 * (w - 1) + j, kperm(16 * w + 4 * g)), zero4);
+  if (w & 1) img_st4(ri, OFF_MQK + 2 * PackedLower::idx(16 * (w - 1) + j, kperm(16 * w + 4 * g)), zero4);
   __syncthreads();  // subtile operands dead, L complete
   SCHED_FENCE();
 
@@ -164,139 +181,153 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitPar
   prep_block_columns<Ar>(sm.L, sm.Tdg, sm.ps.beta, sm.u.INVb, Tww, w, g, j);
   __syncthreads();
   SCHED_FENCE();
-  // INV Diag(beta): staged tile -> image, 16 bytes per lane
-  for (int x = tid; x < CH * CH * 2 / 16; x += FWD_THREADS) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(sm.u.INVb) + 16 * x);
+  // INV Diag(beta): staged 64 x 64 tile -> packed image, one 16-byte chunk
+  // (8 consecutive logical columns) per lane
+  for (int x = tid; x < PackedLower::ELEMS / 8; x += FWD_THREADS) {
+    int r, lc;  // logical row and chunk stored at packed chunk x
+    if (x < PackedLower::TOP / 8) {
+      r = x / 4;
+      lc = (x % 4) ^ PackedLower::Top::sw(r);
+    } else {
+      r = 32 + (x - PackedLower::TOP / 8) / 8;
+      lc = ((x - PackedLower::TOP / 8) % 8) ^ PackedLower::Bot::sw(r - 32);
+    }
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(&sm.u.INVb[TC::idx(r, 8 * lc)]);
     __builtin_amdgcn_raw_buffer_store_b128(v, ri, OFF_INVB + 16 * x, 0, 0);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Recurrence: one workgroup per (document, head, 64-column slice); slices of
-// one (document, head) share an XCD (blockIdx % 8), so the second reads the
-// images from L2.
+// Recurrence: two workgroups per (document, head), each owning 64 state
+// columns; the two share an XCD (blockIdx % 8), so the second copy of a chunk
+// image comes from L2.  A workgroup has 8 waves: waves 0..3 compute (16
+// columns each), waves 4..7 only copy the next chunk's image and v rows into
+// the LDS double buffer and pull later chunks into L2.  A wave stalls while
+// its copies queue up; with the roles split, those stalls fall on the copy
+// wave of each SIMD while the compute wave keeps its MFMA work going.
 // ---------------------------------------------------------------------------
+constexpr int REC_THREADS = 512;
+constexpr int REC_COMPUTE_WAVES = 4;
+constexpr int REC_COPY_THREADS = REC_THREADS - 64 * REC_COMPUTE_WAVES;
+constexpr int SLICE = 64;  // state columns per workgroup
 struct __align__(16) RecSmem {
   ChunkImage buf[2];
-};
-
-// MFMA A-operand fragments of one chunk for one wave, read from the chunk image
-// in LDS ahead of use.  None depends on the state, so the reads of the state
-// path (K_decay, INV, K_restore^T, gamma) are all in flight before the chunk's
-// first product and the chain then runs without waiting on LDS; the output
-// operands (Q_decay, M_qk) are read once the first products are issued, into
-// registers the K_decay fragments free.  Lane (g, j) holds row 16m + j,
-// k elements 32kb + 8g .. +7 of each tile (the k32 operand layout).
-struct StateFrags {
-  bf16x8 kd[4][4];   // K_decay   [m][kb]
-  bf16x8 inv[6];     // INV Diag(beta), blocks (m, kb <= m/2) in m-major order
-  bf16x8 krt[8][2];  // K_restore^T [m][kb]
-  float4 gam[8];     // gamma^C rows 16m + 4g .. +3
-};
-struct OutFrags {
-  bf16x8 qd[4][4];   // Q_decay   [m][kb]
-  bf16x8 mqk[6];     // M_qk, as inv
+  bf16_t V[2][CH * SLICE];  // v rows of the chunk, this workgroup's columns (128 B per token)
+  uint32_t sink[64];        // destination of the L2 prefetch touches; never read
 };
 
 __device__ __forceinline__ bf16x8 frag(const bf16_t *tile, int idx) {
   return *reinterpret_cast<const bf16x8 *>(tile + idx);
 }
-__device__ __forceinline__ void load_state_frags(StateFrags &f, const ChunkImage &im, int g, int j) {
-  using TD = Tile<bf16_t, D>;
-  using TC = Tile<bf16_t, CH>;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) f.kd[m][kb] = frag(im.Kd, TD::idx(16 * m + j, 32 * kb + 8 * g));
-  int x = 0;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) f.inv[x] = frag(im.INVb, TC::idx(16 * m + j, 32 * kb + 8 * g));
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) f.krt[m][kb] = frag(im.KrT, TC::idx(16 * m + j, 32 * kb + 8 * g));
-#pragma unroll
-  for (int m = 0; m < 8; ++m) f.gam[m] = *reinterpret_cast<const float4 *>(&im.gamC[16 * m + 4 * g]);
-}
-__device__ __forceinline__ void load_out_frags(OutFrags &f, const ChunkImage &im, int g, int j) {
-  using TD = Tile<bf16_t, D>;
-  using TC = Tile<bf16_t, CH>;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) f.qd[m][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
-  int x = 0;
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) f.mqk[x] = frag(im.Mqk, TC::idx(16 * m + j, 32 * kb + 8 * g));
-}
-
 __device__ __forceinline__ bf16x8 pack_tiles(floatx4 t0, floatx4 t1) {
   return to_bf16x8(floatx8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]});
 }
 
-// The chunk recurrence (chunk_recurrence in kda_chunk.h) on staged fragments:
+// The chunk recurrence (chunk_recurrence in kda_chunk.h) for this wave's 16
+// state columns, operands from the chunk image in LDS:
 //   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
 //   S <- Diag(gamma^C) S + K_restore^T U.
+// Each phase reads its MFMA A-operand fragments in one batch (lane (g, j): row
+// 16m + j, k elements 32kb + 8g .. +7).
+// O rows go through the bounded descriptor ro (tokens past the chunk are
+// dropped) at byte offset off_o + token * rowb, off_o = (j * H * D + first
+// column of the lane) * 2.
 __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], const floatx4 (&Vt)[4],
-                                         __amdgpu_buffer_rsrc_t ro, int off_v, int rowb, int g,
+                                         __amdgpu_buffer_rsrc_t ro, int off_o, int rowb, int g,
                                          int j) {
-  using IO = bufio<bf16_t>;
-  StateFrags f;
-  load_state_frags(f, im, g, j);
+  using TD = Tile<bf16_t, D>;
+  using TC = Tile<bf16_t, CH>;
+  using PL = PackedLower;
   bf16x8 sb[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) sb[kb] = pack_tiles(S[2 * kb], S[2 * kb + 1]);
+  // U' = V - K_decay S
   floatx4 U[4];
+  {
+    bf16x8 kd[4][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(f.kd[m][kb], sb[kb], x);
-    U[m] = Vt[m] - x;
+      for (int kb = 0; kb < 4; ++kb) kd[m][kb] = frag(im.Kd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(kd[m][kb], sb[kb], x);
+      U[m] = Vt[m] - x;
+    }
   }
-  SCHED_FENCE();
-  OutFrags fo;
-  load_out_frags(fo, im, g, j);
-  bf16x8 bb[2];
+  // U = INV Diag(beta) U'
+  {
+    bf16x8 inv[6];
+    int x = 0;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
-  int x = 0;
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) inv[x] = frag(im.INVb, PL::idx(16 * m + j, 32 * kb + 8 * g));
+    bf16x8 bb[2];
 #pragma unroll
-    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(f.inv[x], bb[kb], acc);
-    U[m] = acc;
+    for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
+    x = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(inv[x], bb[kb], acc);
+      U[m] = acc;
+    }
   }
   bf16x8 ub[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) ub[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
+  // O = Q_decay S + M_qk U, formed transposed: with the operands of each
+  // product swapped, lane (g, j) ends up with token 16m + j, columns 4g..4g+3
+  // of this wave's slice and stores them with one 8-byte write.  Its stores
+  // then complete while the state update runs.
+  {
+    bf16x8 qd[4][4], mqk[6];
+    int x = 0;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    floatx4 acc = S[m];
-    acc[0] *= f.gam[m].x; acc[1] *= f.gam[m].y; acc[2] *= f.gam[m].z; acc[3] *= f.gam[m].w;
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(f.krt[m][kb], ub[kb], acc);
-    S[m] = acc;
+      for (int kb = 0; kb < 4; ++kb) qd[m][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+#pragma unroll
+      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) mqk[x] = frag(im.Mqk, PL::idx(16 * m + j, 32 * kb + 8 * g));
+    }
+    x = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(sb[kb], qd[m][kb], acc);
+#pragma unroll
+      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(ub[kb], mqk[x], acc);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(acc)), ro,
+                                            off_o + (16 * m) * rowb, 0, 0);
+    }
   }
-  x = 0;
+  // S <- Diag(gamma^C) S + K_restore^T U
+  {
+    bf16x8 krt[8][2];
+    float4 gam[8];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(fo.qd[m][kb], sb[kb], acc);
+      for (int kb = 0; kb < 2; ++kb) krt[m][kb] = frag(im.KrT, TC::idx(16 * m + j, 32 * kb + 8 * g));
+      gam[m] = *reinterpret_cast<const float4 *>(&im.gamC[16 * m + 4 * g]);
+    }
 #pragma unroll
-    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(fo.mqk[x], ub[kb], acc);
+    for (int m = 0; m < 8; ++m) {
+      floatx4 acc = S[m];
+      acc[0] *= gam[m].x; acc[1] *= gam[m].y; acc[2] *= gam[m].z; acc[3] *= gam[m].w;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) IO::st1(ro, acc[r], off_v + (16 * m + r) * rowb);
+      for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(krt[m][kb], ub[kb], acc);
+      S[m] = acc;
+    }
   }
 }
 
-__global__ void __launch_bounds__(FWD_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
+__global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
   using IO = bufio<bf16_t>;
   constexpr int ES = 2;
   __shared__ RecSmem sm;
@@ -316,11 +347,79 @@ __global__ void __launch_bounds__(FWD_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uni(tid >> 6);
+  const bool copier = w >= REC_COMPUTE_WAVES;
+  const int H = p.H;
+  const int rowb = H * D * ES;
+  const int nch = (int)((b - a + CH - 1) / CH);
+
+  if (copier) {
+    // ---------------- copy waves ----------------
+    const int cw = w - REC_COMPUTE_WAVES;                // 0..3
+    const int ct = tid - 64 * REC_COMPUTE_WAVES;         // 0..255
+    const bf16_t *v = (const bf16_t *)p.v;
+    const char *img0 = (const char *)p.ws + ((int64_t)h * p.n_slots + first_slot(a, d)) * IMG_BYTES;
+    const uint32_t lds_img = lds_addr(&sm.buf[0]);
+    const uint32_t lds_v = lds_addr(&sm.V[0][0]);
+    const uint32_t lds_sink = lds_addr(&sm.sink[0]);
+    // v rows of chunk kk, this workgroup's columns; rows past the chunk (or a
+    // chunk past the document) read 0
+    auto v_rsrc = [&](int kk) {
+      const int64_t c0 = a + (int64_t)kk * CH;
+      const int n = (kk < nch) ? (int)min((int64_t)CH, b - c0) : 0;
+      const int bytes = n > 0 ? ((n - 1) * H * D + SLICE) * ES : 0;
+      return rsrc_words(v + (c0 * H + h) * D + split * SLICE, bytes);
+    };
+    // chunk kk -> buffer kk & 1: v in 1 KB blocks of 8 token rows (blocks cw and
+    // cw + 4), the image in 1 KB blocks cw, cw + 4, ...
+    auto issue_copy = [&](int kk) {
+      const i32x4 rv = v_rsrc(kk);
+      const uint32_t vdst = lds_v + (uint32_t)((kk & 1) * CH * SLICE * ES);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int blk = cw + 4 * i;
+        copy16_to_lds(rv, vdst + blk * 1024, (8 * blk + (lane >> 3)) * rowb + (lane & 7) * 16);
+      }
+      const i32x4 ri = rsrc_words(img0 + (int64_t)kk * IMG_BYTES, IMG_BYTES);
+      const uint32_t dst = lds_img + (uint32_t)((kk & 1) * IMG_BYTES);
+      for (int blk = cw; blk < IMG_BLOCKS; blk += 4) copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
+    };
+    // L2 prefetch of chunk kk: this slice's half of the image and its v rows,
+    // one dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
+    // (offsets past the data, or a chunk past the document, fetch nothing), so
+    // the wait at the top of the loop can leave exactly these in flight.
+    constexpr int TOUCH_OPS = 3;
+    constexpr int OOB = 1 << 30;
+    constexpr int HALF = IMG_BYTES / 2;
+    static_assert(HALF / 64 <= 2 * REC_COPY_THREADS && 2 * CH <= REC_COPY_THREADS, "touch coverage");
+    auto issue_touch = [&](int kk) {
+      const i32x4 ri = rsrc_words(img0 + (int64_t)kk * IMG_BYTES, kk < nch ? IMG_BYTES : 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int idx = i * REC_COPY_THREADS + ct;
+        touch4_to_lds(ri, lds_sink, idx < HALF / 64 ? split * HALF + idx * 64 : OOB);
+      }
+      touch4_to_lds(v_rsrc(kk), lds_sink, ct < 2 * CH ? (ct >> 1) * rowb + (ct & 1) * 64 : OOB);
+    };
+    constexpr int AHEAD = 2;  // chunks between a touch and the copy that uses it
+
+    issue_copy(0);
+    for (int kk = 1; kk < AHEAD; ++kk) issue_touch(kk);
+    for (int kk = 0; kk < nch; ++kk) {
+      // this wave's copy of chunk kk has landed (only the last touches may still
+      // be in flight); after the barrier buffer (kk + 1) & 1 is free
+      wait_vmem_except_last<TOUCH_OPS>();
+      lds_barrier();
+      if (kk + 1 < nch) issue_copy(kk + 1);
+      issue_touch(kk + AHEAD);
+    }
+    wait_vmem();  // no copy may still target this workgroup's LDS when it exits
+    return;
+  }
+
+  // ---------------- compute waves ----------------
   const int g = lane >> 4;
   const int j = lane & 15;
-  const int colW = split * 64 + w * 16;
-  const int H = p.H;
-
+  const int colW = split * SLICE + 16 * w;
   floatx4 S[8];
   if (p.init) {
     state_load(S, uniptr(p.init + ((int64_t)d * H + h) * (D * D)), D, colW, g, j);
@@ -328,50 +427,20 @@ __global__ void __launch_bounds__(FWD_THREADS, 1) kda_chunk_rec_kernel(SplitPara
 #pragma unroll
     for (int m = 0; m < 8; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-
-  const bf16_t *v = (const bf16_t *)p.v;
   bf16_t *o = (bf16_t *)p.o;
-  const int rowb = H * D * ES;
-  const int off_v = (4 * g * H * D + colW + j) * ES;
-  const int nch = (int)((b - a + CH - 1) / CH);
-  const char *img0 = (const char *)p.ws + ((int64_t)h * p.n_slots + first_slot(a, d)) * IMG_BYTES;
-  const uint32_t lds0 = lds_addr(&sm.buf[0]);
-
-  // image of chunk kk -> buffer kk & 1, 1 KB blocks dealt round-robin to the waves
-  auto issue_image = [&](int kk) {
-    const i32x4 rs = rsrc_words(img0 + (int64_t)kk * IMG_BYTES, IMG_BYTES);
-    const uint32_t dst = lds0 + (uint32_t)((kk & 1) * IMG_BYTES);
-    for (int blk = w; blk < IMG_BLOCKS; blk += 4) copy16_to_lds(rs, dst + blk * 1024, lane * 16 + blk * 1024);
-  };
-  typename IO::raw1 Rv[4][4];
-  auto fetch_v = [&](int kk) {
-    const int64_t c0 = a + (int64_t)kk * CH;
-    const int n = (int)min((int64_t)CH, b - c0);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (c0 * H + h) * D, ((n - 1) * H + 1) * D * ES);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Rv[m][r] = IO::ld1(rv, off_v + (16 * m + r) * rowb);
-  };
-
-  issue_image(0);
-  fetch_v(0);
+  const int off_o = (j * H * D + colW + 4 * g) * ES;  // token j, columns 4g..4g+3
   for (int kk = 0; kk < nch; ++kk) {
     const int64_t cs = a + (int64_t)kk * CH;
     const int len = (int)min((int64_t)CH, b - cs);
-    wait_vmem();      // this wave's copies of image kk (and V of chunk kk) have landed
-    __syncthreads();  // ... and every wave's; buffer (kk + 1) & 1 is no longer read
+    lds_barrier();  // the copy of chunk kk is complete in buffer kk & 1
     floatx4 Vt[4];
+    const bf16_t *vb = &sm.V[kk & 1][0];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Vt[m][r] = IO::cvt1(Rv[m][r]);
-    if (kk + 1 < nch) {
-      issue_image(kk + 1);
-      fetch_v(kk + 1);
-    }
+      for (int r = 0; r < 4; ++r) Vt[m][r] = bf16_to_f32(vb[(16 * m + 4 * g + r) * SLICE + 16 * w + j]);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + (cs * H + h) * D, ((len - 1) * H + 1) * D * ES);
-    rec_step(sm.buf[kk & 1], S, Vt, ro, off_v, rowb, g, j);
+    rec_step(sm.buf[kk & 1], S, Vt, ro, off_o, rowb, g, j);
   }
   if (p.final_state) state_store(S, uniptr(p.final_state + ((int64_t)d * H + h) * (D * D)), D, colW, g, j);
 }
@@ -387,9 +456,8 @@ hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
-  const int units = p.N * p.H;
-  const int groups = (units + 7) / 8;
-  hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * 2)), dim3(FWD_THREADS), 0, stream, p);
+  const int groups = (p.N * p.H + 7) / 8;  // two slices per (document, head), XCD-paired
+  hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * 2)), dim3(REC_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 

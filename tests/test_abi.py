@@ -112,10 +112,10 @@ def test_segment_scan_workspace_checks(lib):
 
 
 def test_chunk_fwd_workspace_checks(lib):
-    # one 65 KiB chunk image per head and slot, floor(T / 64) + N slots per head
+    # one 62 KiB chunk image per head and slot, floor(T / 64) + N slots per head
     need = lib.kda_chunk_fwd_workspace_size(1, 128, 4, 128, 128)
-    assert need == (128 // 64 + 1) * 4 * 66560
-    assert lib.kda_chunk_fwd_workspace_size(3, 1000, 2, 128, 128) == (1000 // 64 + 3) * 2 * 66560
+    assert need == (128 // 64 + 1) * 4 * 63488
+    assert lib.kda_chunk_fwd_workspace_size(3, 1000, 2, 128, 128) == (1000 // 64 + 3) * 2 * 63488
     assert lib.kda_chunk_fwd_workspace_size(0, 128, 4, 128, 128) == 0
     assert lib.kda_chunk_fwd_workspace_size(1, 128, 4, 64, 128) == 0
     # the two-kernel path (bf16, compute AUTO) refuses a short or misaligned workspace
