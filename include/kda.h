@@ -139,20 +139,25 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
 /* kda_segment_scan -- intra-device context parallelism for long prefill.
  *
  * Same operator and arguments as kda_chunk_fwd.  The packed sequence is cut into
- * n_segments equal token ranges (the last one ragged).  Following equation (17)
- * of the systems page and its derivation (section "公式 (17) 的推导"):
+ * n_segments segments.  Following equation (17) of the systems page and its
+ * derivation (section "公式 (17) 的推导"):
  *   A. each (segment, head) computes its affine pair (M, S~) from a zero state
  *      (M = product of the per-token transitions; M = 0 when a document starts
  *      inside the segment, whose S~ then starts from that document's state);
- *   B. per head, entry states are scanned: E_0 = S0, E_{j+1} = M_j E_j + S~_j,
- *      reset to the document's initial state where a document starts exactly on
- *      a segment boundary;
+ *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j;
  *   C. every segment is re-run from its exact entry state, producing O and the
  *      final state of every document.
+ * With bf16 arithmetic (dtype KDA_BF16, compute AUTO) the segments are equal
+ * ranges of 64-token chunk slots (see kda_chunk_fwd_workspace_size) and all
+ * three phases run on the two kernels of kda_chunk_fwd over one chunk prep;
+ * with fp32 arithmetic they are equal token ranges (the last one ragged) run by
+ * the fused kernel, and a document starting exactly on a segment boundary
+ * resets the scan to its initial state.
  * n_segments <= 0 means one segment per compute unit of the current device.
  * workspace: device memory of at least kda_segment_scan_workspace_size() bytes,
  * 256-byte aligned; its contents on entry are ignored. */
-size_t kda_segment_scan_workspace_size(int32_t n_segments, int32_t H, int32_t dk, int32_t dv);
+size_t kda_segment_scan_workspace_size(int32_t N, int64_t T, int32_t H, int32_t n_segments,
+                                       int32_t dk, int32_t dv);
 
 int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_logits,
                      const void *beta, const float *A_log, float g_min,

@@ -47,6 +47,11 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with linear_attention_fwd_amd._build.build()")
+    # PyTorch ships its own HIP runtime.  Import it first so that libkda.so binds
+    # to that runtime (same soname, already loaded) instead of loading a second
+    # one from /opt/rocm: with two HIP runtimes in one process whichever
+    # initialises second finds no GPU.
+    _torch()
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
@@ -62,7 +67,7 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_recurrence.restype = ctypes.c_int
     lib.kda_segment_scan.argtypes = prefill + [i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_segment_scan.restype = ctypes.c_int
-    lib.kda_segment_scan_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.kda_segment_scan_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.kda_segment_scan_workspace_size.restype = ctypes.c_size_t
     lib.kda_default_segments.argtypes = []
     lib.kda_default_segments.restype = ctypes.c_int
@@ -229,8 +234,9 @@ def kda_chunk_recurrence(v, workspace, initial_state=None, cu_seqlens=None, cu_s
     return o, final_state
 
 
-def kda_segment_scan_workspace_size(n_segments: int, H: int, dk: int = 128, dv: int = 128) -> int:
-    return int(load_library().kda_segment_scan_workspace_size(n_segments, H, dk, dv))
+def kda_segment_scan_workspace_size(N: int, T: int, H: int, n_segments: int = 0, dk: int = 128,
+                                    dv: int = 128) -> int:
+    return int(load_library().kda_segment_scan_workspace_size(N, T, H, n_segments, dk, dv))
 
 
 def kda_default_segments() -> int:
@@ -253,10 +259,7 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
                                                        initial_state, cu_seqlens, cu_seqlens_host)
     n_seg = n_segments if n_segments > 0 else kda_default_segments()
-    n_seg = max(1, min(n_seg, max(T, 1)))
-    seg_len = -(-max(T, 1) // n_seg)
-    n_seg = -(-max(T, 1) // seg_len)
-    need = kda_segment_scan_workspace_size(n_seg, H, dk, dv)
+    need = kda_segment_scan_workspace_size(N, T, H, n_seg, dk, dv)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if o is None:

@@ -112,6 +112,24 @@ size_t scan_workspace(int64_t n_seg, int64_t H) {
   return (size_t)n_seg * H * kD * (3 * kD) * sizeof(float);  // pairs [., 2D] + entry [., D]
 }
 
+// Segment plans.  The fused path (fp32 arithmetic) cuts the tokens into n_seg
+// equal ranges; the two-kernel path cuts the chunk slots into n_seg equal
+// ranges.  Both clamp the count so that no segment is empty.
+struct SegPlan {
+  int64_t n_seg, len;  // number of segments and tokens (fused) or slots (two-kernel) per segment
+};
+SegPlan plan_segments(int64_t units, int64_t requested) {
+  int64_t n = requested;
+  if (n > units) n = units;
+  if (n < 1) n = 1;
+  const int64_t len = (units + n - 1) / n;
+  return SegPlan{(units + len - 1) / len, len};
+}
+size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
+  const SegPlan sp = plan_segments(kda::n_chunk_slots(T, N), requested);
+  return kda::split_workspace_bytes(T, N, H) + scan_workspace(sp.n_seg, H);
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,9 +248,19 @@ int kda_default_segments(void) {
   return cus;
 }
 
-size_t kda_segment_scan_workspace_size(int32_t n_segments, int32_t H, int32_t dk, int32_t dv) {
-  if (n_segments <= 0 || H <= 0 || dk != kD || dv != kD) return 0;
-  return scan_workspace(n_segments, H);
+size_t kda_segment_scan_workspace_size(int32_t N, int64_t T, int32_t H, int32_t n_segments,
+                                       int32_t dk, int32_t dv) {
+  if (N <= 0 || T < 0 || H <= 0 || dk != kD || dv != kD) return 0;
+  int64_t req = n_segments;
+  if (req <= 0) {
+    const int cus = kda_default_segments();
+    if (cus < 0) return 0;
+    req = cus;
+  }
+  // enough for either arithmetic path
+  const size_t fused = scan_workspace(plan_segments(T > 0 ? T : 1, req).n_seg, H);
+  const size_t split = split_scan_workspace(T, N, H, req);
+  return fused > split ? fused : split;
 }
 
 int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_logits,
@@ -247,39 +275,69 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   if (rc != KDA_OK) return rc;
   if (final_state && initial_state && final_state == initial_state)
     return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not alias initial_state");
-  int64_t n_seg = n_segments;
-  if (n_seg <= 0) {
+  int64_t req = n_segments;
+  if (req <= 0) {
     const int cus = kda_default_segments();
     if (cus < 0) return cus;
-    n_seg = cus;
+    req = cus;
   }
+  const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   hipStream_t st = (hipStream_t)stream;
-  if (T > 0) {
-    if (n_seg > T) n_seg = T;
-    const int64_t seg_len = (T + n_seg - 1) / n_seg;
-    n_seg = (T + seg_len - 1) / seg_len;  // no empty segment
-    if (n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
-    const size_t need = scan_workspace(n_seg, H);
+  if (T > 0 && !f32c) {
+    // two-kernel path: chunk prep over all chunks, segment pairs and the re-run
+    // on the recurrence kernel; segments are ranges of chunk slots
+    const int64_t n_slots = kda::n_chunk_slots(T, N);
+    if (n_slots * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
+    const SegPlan sp = plan_segments(n_slots, req);
+    if (sp.n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
+    const size_t need = split_scan_workspace(T, N, H, req);
+    if (!workspace || workspace_bytes < need)
+      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    float *pairs = (float *)((char *)workspace + kda::split_workspace_bytes(T, N, H));
+    float *entry = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
+
+    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
+                                      cu_seqlens, N, T, H, o, final_state, workspace);
+    p.n_seg = (int)sp.n_seg;
+    p.seg_slots = sp.len;
+    p.entry = entry;
+    p.pairs = pairs;
+    hipError_t e = kda::launch_chunk_prep(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan prep");
+    p.rmode = 2;  // A: segment pairs; resets at document starts are folded into them
+    e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
+    // B: entry states E_0 = 0, E_{j+1} = M_j E_j + S~_j (the first chunk is a
+    // document start, so E_0 never matters)
+    e = kda::launch_pair_scan(pairs, nullptr, nullptr, 1, T, H, (int)sp.n_seg, 0, entry, false, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
+    p.rmode = 1;  // C: re-run every segment from its exact entry state
+    e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
+  } else if (T > 0) {
+    const SegPlan sp = plan_segments(T, req);
+    if (sp.n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
+    const size_t need = scan_workspace(sp.n_seg, H);
     if (!workspace || workspace_bytes < need)
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     float *pairs = (float *)workspace;
-    float *entry = pairs + (size_t)n_seg * H * kD * 2 * kD;
+    float *entry = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
     const bool bf16_in = dtype == KDA_BF16;
-    const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
 
     kda::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
     p.A_log = A_log; p.g_min = g_min;
     p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
-    p.n_items = (int)n_seg; p.seg_len = seg_len;
+    p.n_items = (int)sp.n_seg; p.seg_len = sp.len;
     p.doc_init = initial_state;
     // A: segment pairs (M, S~)
     p.mode = 2; p.item_init = nullptr; p.o = nullptr; p.final_state = pairs;
     hipError_t e = kda::launch_fwd(p, bf16_in, f32c, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states
-    e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, T, H, (int)n_seg, seg_len,
+    e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, T, H, (int)sp.n_seg, sp.len,
                               entry, f32c, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
     // C: re-run every segment from its exact entry state

@@ -56,6 +56,14 @@ struct SplitParams {
   float *final_state;      // [N, H, D, D] or nullptr
   void *ws;                // chunk images [H, n_slots, image]
   int64_t n_slots;         // chunk slots per head (see first_slot)
+  // recurrence work split: 0 = one item per document; 1 = segment re-run from
+  // entry states; 2 = segment pairs (M, S~).  Segments are ranges of seg_slots
+  // chunk slots.
+  int rmode;
+  int n_seg;
+  int64_t seg_slots;
+  const float *entry;      // mode 1: entry state per segment [n_seg, H, D, D]
+  float *pairs;            // mode 2: [n_seg, H, D, 2D], columns 0..127 S~, 128..255 M
 };
 size_t split_workspace_bytes(int64_t T, int N, int H);
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);

@@ -327,22 +327,67 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], 
   }
 }
 
+// The chunk a slot holds: document d, first token cs, len tokens (0: no chunk
+// maps to the slot), whether it starts and whether it ends its document.
+struct SlotChunk {
+  int d;
+  int64_t cs;
+  int len;
+  bool first, last;
+};
+__device__ __forceinline__ SlotChunk slot_chunk(const SplitParams &p, int64_t slot) {
+  SlotChunk c;
+  c.d = doc_of_slot(p.cu, p.N, slot);
+  const int64_t a = uni64(cu_at(p.cu, p.T, c.d));
+  const int64_t b = uni64(cu_at(p.cu, p.T, c.d + 1));
+  c.cs = a + (slot - first_slot(a, c.d)) * CH;
+  c.len = c.cs < b ? (int)min((int64_t)CH, b - c.cs) : 0;
+  c.first = c.cs == a;
+  c.last = c.cs + c.len == b;
+  return c;
+}
+// first slot in [s, s_end) that holds a chunk, or s_end
+__device__ __forceinline__ int64_t next_chunk_slot(const SplitParams &p, int64_t s, int64_t s_end) {
+  while (s < s_end && slot_chunk(p, s).len == 0) ++s;
+  return s;
+}
+
+// One workgroup per (item, head, 64-column slice).  Items: documents (rmode 0),
+// or segments of seg_slots chunk slots (rmode 1: re-run from the segment's
+// entry state, writing O and the final states of documents ending inside;
+// rmode 2: the segment's pair, state [S~ | M] from [0 | I] with v = 0 on the
+// M columns, four slices).  At the first chunk of a document the state is
+// reset to that document's initial state (M columns: 0), so a pair whose
+// segment contains a document start has M = 0 and the scan needs no document
+// logic.
 __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
   using IO = bufio<bf16_t>;
   constexpr int ES = 2;
   __shared__ RecSmem sm;
 
-  const int units = p.N * p.H;
+  const int nsplit = p.rmode == 2 ? 4 : 2;
+  const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
   const int xlo = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
-  const int split = rest & 1;
-  const int unit = (rest >> 1) * 8 + xlo;
+  const int split = rest % nsplit;
+  const int unit = (rest / nsplit) * 8 + xlo;
   if (unit >= units) return;
-  const int d = unit / p.H;
+  const int item = unit / p.H;
   const int h = unit % p.H;
-  const int64_t a = uni64(cu_at(p.cu, p.T, d));
-  const int64_t b = uni64(cu_at(p.cu, p.T, d + 1));
-  if (a == b) return;  // empty documents are handled by kda_copy_empty_kernel
+  int64_t s_begin, s_end;
+  if (p.rmode == 0) {
+    const int64_t a = uni64(cu_at(p.cu, p.T, item));
+    const int64_t b = uni64(cu_at(p.cu, p.T, item + 1));
+    if (a == b) return;  // empty documents are handled by kda_copy_empty_kernel
+    s_begin = first_slot(a, item);
+    s_end = s_begin + (b - a + CH - 1) / CH;
+  } else {
+    s_begin = (int64_t)item * p.seg_slots;
+    s_end = min(s_begin + p.seg_slots, p.n_slots);
+  }
+  s_begin = uni64(s_begin);
+  s_end = uni64(s_end);
+  const bool m_cols = p.rmode == 2 && split >= 2;  // M columns of a pair: v = 0, start from I
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -350,67 +395,70 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   const bool copier = w >= REC_COMPUTE_WAVES;
   const int H = p.H;
   const int rowb = H * D * ES;
-  const int nch = (int)((b - a + CH - 1) / CH);
 
   if (copier) {
     // ---------------- copy waves ----------------
     const int cw = w - REC_COMPUTE_WAVES;                // 0..3
     const int ct = tid - 64 * REC_COMPUTE_WAVES;         // 0..255
     const bf16_t *v = (const bf16_t *)p.v;
-    const char *img0 = (const char *)p.ws + ((int64_t)h * p.n_slots + first_slot(a, d)) * IMG_BYTES;
+    const char *img_h = (const char *)p.ws + (int64_t)h * p.n_slots * IMG_BYTES;
     const uint32_t lds_img = lds_addr(&sm.buf[0]);
     const uint32_t lds_v = lds_addr(&sm.V[0][0]);
     const uint32_t lds_sink = lds_addr(&sm.sink[0]);
-    // v rows of chunk kk, this workgroup's columns; rows past the chunk (or a
-    // chunk past the document) read 0
-    auto v_rsrc = [&](int kk) {
-      const int64_t c0 = a + (int64_t)kk * CH;
-      const int n = (kk < nch) ? (int)min((int64_t)CH, b - c0) : 0;
-      const int bytes = n > 0 ? ((n - 1) * H * D + SLICE) * ES : 0;
-      return rsrc_words(v + (c0 * H + h) * D + split * SLICE, bytes);
+    // v rows of a chunk, this workgroup's columns; rows past the chunk (and all
+    // of them for M columns or past the range) read 0
+    auto v_rsrc = [&](const SlotChunk &c, bool in_range) {
+      const int bytes = (in_range && !m_cols && c.len > 0) ? ((c.len - 1) * H * D + SLICE) * ES : 0;
+      return rsrc_words(v + (c.cs * H + h) * D + (split & 1) * SLICE, bytes);
     };
-    // chunk kk -> buffer kk & 1: v in 1 KB blocks of 8 token rows (blocks cw and
-    // cw + 4), the image in 1 KB blocks cw, cw + 4, ...
-    auto issue_copy = [&](int kk) {
-      const i32x4 rv = v_rsrc(kk);
+    // chunk of slot sl -> buffer kk & 1: v in 1 KB blocks of 8 token rows
+    // (blocks cw and cw + 4), the image in 1 KB blocks cw, cw + 4, ...
+    auto issue_copy = [&](int64_t sl, int kk) {
+      const SlotChunk c = slot_chunk(p, sl);
+      const i32x4 rv = v_rsrc(c, true);
       const uint32_t vdst = lds_v + (uint32_t)((kk & 1) * CH * SLICE * ES);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int blk = cw + 4 * i;
         copy16_to_lds(rv, vdst + blk * 1024, (8 * blk + (lane >> 3)) * rowb + (lane & 7) * 16);
       }
-      const i32x4 ri = rsrc_words(img0 + (int64_t)kk * IMG_BYTES, IMG_BYTES);
+      const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, IMG_BYTES);
       const uint32_t dst = lds_img + (uint32_t)((kk & 1) * IMG_BYTES);
       for (int blk = cw; blk < IMG_BLOCKS; blk += 4) copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
     };
-    // L2 prefetch of chunk kk: this slice's half of the image and its v rows,
+    // L2 prefetch of slot sl: this slice's half of the image and its v rows,
     // one dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
-    // (offsets past the data, or a chunk past the document, fetch nothing), so
-    // the wait at the top of the loop can leave exactly these in flight.
+    // (offsets past the data, or a slot past the range, fetch nothing), so the
+    // wait at the top of the loop can leave exactly these in flight.
     constexpr int TOUCH_OPS = 3;
     constexpr int OOB = 1 << 30;
     constexpr int HALF = IMG_BYTES / 2;
     static_assert(HALF / 64 <= 2 * REC_COPY_THREADS && 2 * CH <= REC_COPY_THREADS, "touch coverage");
-    auto issue_touch = [&](int kk) {
-      const i32x4 ri = rsrc_words(img0 + (int64_t)kk * IMG_BYTES, kk < nch ? IMG_BYTES : 0);
+    auto issue_touch = [&](int64_t sl) {
+      const bool in_range = sl < s_end;
+      const SlotChunk c = slot_chunk(p, in_range ? sl : s_begin);
+      const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, in_range ? IMG_BYTES : 0);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int idx = i * REC_COPY_THREADS + ct;
-        touch4_to_lds(ri, lds_sink, idx < HALF / 64 ? split * HALF + idx * 64 : OOB);
+        touch4_to_lds(ri, lds_sink, idx < HALF / 64 ? (split & 1) * HALF + idx * 64 : OOB);
       }
-      touch4_to_lds(v_rsrc(kk), lds_sink, ct < 2 * CH ? (ct >> 1) * rowb + (ct & 1) * 64 : OOB);
+      touch4_to_lds(v_rsrc(c, in_range), lds_sink, ct < 2 * CH ? (ct >> 1) * rowb + (ct & 1) * 64 : OOB);
     };
-    constexpr int AHEAD = 2;  // chunks between a touch and the copy that uses it
+    constexpr int AHEAD = 2;  // slots between a touch and the copy that uses it
 
-    issue_copy(0);
-    for (int kk = 1; kk < AHEAD; ++kk) issue_touch(kk);
-    for (int kk = 0; kk < nch; ++kk) {
-      // this wave's copy of chunk kk has landed (only the last touches may still
-      // be in flight); after the barrier buffer (kk + 1) & 1 is free
+    int64_t sl = next_chunk_slot(p, s_begin, s_end);
+    if (sl < s_end) issue_copy(sl, 0);
+    for (int i = 1; i < AHEAD; ++i) issue_touch(sl + i);
+    for (int kk = 0; sl < s_end; ++kk) {
+      const int64_t nsl = next_chunk_slot(p, sl + 1, s_end);
+      // this wave's copy of the current chunk has landed (only the last touches
+      // may still be in flight); after the barrier buffer (kk + 1) & 1 is free
       wait_vmem_except_last<TOUCH_OPS>();
       lds_barrier();
-      if (kk + 1 < nch) issue_copy(kk + 1);
-      issue_touch(kk + AHEAD);
+      if (nsl < s_end) issue_copy(nsl, kk + 1);
+      issue_touch(sl + AHEAD);
+      sl = nsl;
     }
     wait_vmem();  // no copy may still target this workgroup's LDS when it exits
     return;
@@ -421,28 +469,44 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   const int j = lane & 15;
   const int colW = split * SLICE + 16 * w;
   floatx4 S[8];
-  if (p.init) {
-    state_load(S, uniptr(p.init + ((int64_t)d * H + h) * (D * D)), D, colW, g, j);
+  if (p.rmode == 1) {
+    state_load(S, uniptr(p.entry + ((int64_t)item * H + h) * (D * D)), D, colW, g, j);
   } else {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[m][r] = (m_cols && 16 * m + 4 * g + r == colW + j - D) ? 1.f : 0.f;
   }
   bf16_t *o = (bf16_t *)p.o;
   const int off_o = (j * H * D + colW + 4 * g) * ES;  // token j, columns 4g..4g+3
-  for (int kk = 0; kk < nch; ++kk) {
-    const int64_t cs = a + (int64_t)kk * CH;
-    const int len = (int)min((int64_t)CH, b - cs);
-    lds_barrier();  // the copy of chunk kk is complete in buffer kk & 1
+  int64_t sl = next_chunk_slot(p, s_begin, s_end);
+  for (int kk = 0; sl < s_end; ++kk) {
+    const int64_t nsl = next_chunk_slot(p, sl + 1, s_end);
+    const SlotChunk c = slot_chunk(p, sl);
+    lds_barrier();  // the copy of this chunk is complete in buffer kk & 1
+    if (c.first) {  // a document starts: its initial state (M columns: 0)
+      if (!m_cols && p.init) {
+        state_load(S, uniptr(p.init + ((int64_t)c.d * H + h) * (D * D)), D, colW, g, j);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
     floatx4 Vt[4];
     const bf16_t *vb = &sm.V[kk & 1][0];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) Vt[m][r] = bf16_to_f32(vb[(16 * m + 4 * g + r) * SLICE + 16 * w + j]);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + (cs * H + h) * D, ((len - 1) * H + 1) * D * ES);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(o + (c.cs * H + h) * D, p.rmode != 2 ? ((c.len - 1) * H + 1) * D * ES : 0);
     rec_step(sm.buf[kk & 1], S, Vt, ro, off_o, rowb, g, j);
+    if (c.last && p.rmode != 2 && p.final_state)
+      state_store(S, uniptr(p.final_state + ((int64_t)c.d * H + h) * (D * D)), D, colW, g, j);
+    sl = nsl;
   }
-  if (p.final_state) state_store(S, uniptr(p.final_state + ((int64_t)d * H + h) * (D * D)), D, colW, g, j);
+  if (p.rmode == 2)  // the segment's pair [S~ | M]
+    state_store(S, uniptr(p.pairs + ((int64_t)item * H + h) * (D * 2 * D)), 2 * D, colW, g, j);
 }
 
 size_t split_workspace_bytes(int64_t T, int N, int H) {
@@ -456,8 +520,13 @@ hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
-  const int groups = (p.N * p.H + 7) / 8;  // two slices per (document, head), XCD-paired
-  hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * 2)), dim3(REC_THREADS), 0, stream, p);
+  // slices of one (item, head) share an XCD: two for documents and re-runs,
+  // four for pairs
+  const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
+  const int groups = (units + 7) / 8;
+  const int nsplit = p.rmode == 2 ? 4 : 2;
+  hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * nsplit)), dim3(REC_THREADS), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

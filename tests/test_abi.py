@@ -100,13 +100,22 @@ def test_prefill_validation(lib, fn):
 
 def test_segment_scan_workspace_checks(lib):
     # explicit segment count: a short or missing workspace is refused before any launch
-    need = lib.kda_segment_scan_workspace_size(4, 4, 128, 128)
-    assert need == 4 * 4 * 128 * 384 * 4
-    assert lib.kda_segment_scan_workspace_size(0, 4, 128, 128) == 0
-    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=None, ws_bytes=0) == KDA_ERR_WORKSPACE
-    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=FAKE, ws_bytes=need - 1) == KDA_ERR_WORKSPACE
-    assert _prefill(lib, "kda_segment_scan", nseg=4, ws=ctypes.c_void_p(0x1004), ws_bytes=need) \
-        == KDA_ERR_WORKSPACE
+    # enough for either path: chunk images + pairs + entry states of the chunk-slot
+    # segments (bf16), or pairs + entry states of the token segments (fp32)
+    need = lib.kda_segment_scan_workspace_size(1, 128, 4, 4, 128, 128)
+    slots = 128 // 64 + 1                                    # 3 chunk slots -> 3 segments
+    need_bf16 = slots * 4 * 63488 + 3 * 4 * 128 * 384 * 4    # images + pairs + entry states
+    need_f32 = 4 * 4 * 128 * 384 * 4                         # 4 token segments
+    assert need == max(need_bf16, need_f32)
+    assert lib.kda_segment_scan_workspace_size(0, 128, 4, 4, 128, 128) == 0
+    assert lib.kda_segment_scan_workspace_size(1, 128, 4, 4, 64, 128) == 0
+    for compute, req in ((0, need_bf16), (1, need_f32)):  # bf16 inputs, both arithmetic paths
+        assert _prefill(lib, "kda_segment_scan", nseg=4, compute=compute, ws=None,
+                        ws_bytes=0) == KDA_ERR_WORKSPACE
+        assert _prefill(lib, "kda_segment_scan", nseg=4, compute=compute, ws=FAKE,
+                        ws_bytes=req - 1) == KDA_ERR_WORKSPACE
+        assert _prefill(lib, "kda_segment_scan", nseg=4, compute=compute,
+                        ws=ctypes.c_void_p(0x1004), ws_bytes=req) == KDA_ERR_WORKSPACE
     assert _prefill(lib, "kda_segment_scan", nseg=4, S0=FAKE, fin=FAKE, ws=FAKE,
                     ws_bytes=need) == KDA_ERR_UNSUPPORTED
 
@@ -175,3 +184,17 @@ def test_decode_validation(lib):
     assert call(g_min=-6.0) == KDA_ERR_GATE_BOUND
     assert call(N=0) == KDA_OK                   # nothing to do, nothing launched
     assert lib.kda_last_error() is not None
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before torch has touched anything must not bring in a
+    second HIP runtime (PyTorch ships its own; with two in one process the one
+    initialised second sees no GPU)."""
+    code = ("import os, linear_attention_fwd_amd as kda\n"
+            "kda.load_library()\n"
+            "import torch\n"
+            "maps = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "print(len(set(l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l)))\n")
+    out = subprocess.run([__import__("sys").executable, "-c", code], capture_output=True,
+                         text=True, cwd=ROOT, check=True).stdout
+    assert out.strip() == "1", out

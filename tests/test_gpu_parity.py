@@ -158,10 +158,16 @@ def test_segment_scan_matches_oracle(name, n_seg):
 
 
 def test_segment_scan_one_segment_equals_chunk_fwd():
+    """One segment re-runs every chunk from the start: with bf16 arithmetic the
+    recurrence kernel of the two-kernel chunk_fwd, with fp32 arithmetic the fused
+    kernel, in both cases bit for bit."""
     inp = kda_gen.make_prefill(44, 640, 2, "bf16", lengths=[200, 440], s0_std=0.02,
                                s0_docs="all")
-    o1, S1 = gpu_chunk_fwd(inp, fused=True)
+    o1, S1 = gpu_chunk_fwd(inp)
     o2, S2 = gpu_segment_scan(inp, n_segments=1)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    o1, S1 = gpu_chunk_fwd(inp, compute=1)
+    o2, S2 = gpu_segment_scan(inp, n_segments=1, compute=1)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
