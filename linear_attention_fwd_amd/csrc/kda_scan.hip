@@ -10,7 +10,9 @@
 // One workgroup per (head, 16-column slice of the state); columns of E never
 // mix in E <- M E + S~, so slices are independent.  Each of the 4 waves owns
 // 32 rows of E; the current E slice is shared through LDS (transposed so a
-// lane's B operand is one contiguous read).  With bf16 arithmetic the product
+// lane's B operand is one contiguous read, double-buffered so one barrier per
+// step suffices).  The scan is serial over segments, so each step's pair is
+// loaded during the previous step.  With bf16 arithmetic the product
 // uses a hi/lo split of both operands (three MFMAs, about 16 mantissa bits),
 // since errors in M E would otherwise propagate along the whole scan; the fp32
 // verification build uses fp32 MFMA.
@@ -31,12 +33,21 @@ __device__ __forceinline__ int scan_doc_of(const int32_t *cu, int N, int64_t pos
   return lo;
 }
 
+// The operands of one scan step for this lane: rows 32w + 16t + j of M (the
+// A operand, 8 consecutive columns per k block) and S~ at rows 32w + 16t + 4g
+// + r, column col.  They do not depend on E, so the next step's are loaded
+// while the current step computes.
+struct ScanOps {
+  float4 m[2][4][2];  // [t][kb][half]
+  floatx4 st[2];
+};
+
 template <bool F32C>
 __global__ void __launch_bounds__(SCAN_THREADS, 1)
 kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ S0,
                      const int32_t *__restrict__ cu, int N, int H, int n_seg, int64_t seg_len,
                      float *__restrict__ entry) {
-  __shared__ __align__(16) float ET[16][D];  // E slice, [column][row]
+  __shared__ __align__(16) float ET[2][16][D];  // E slice, [buffer][column][row]
 
   const int h = blockIdx.x / 8;
   const int cs = blockIdx.x % 8;
@@ -61,64 +72,90 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         dst[row_of(t, r) * D + col] = E[t][r];
-        ET[j][row_of(t, r)] = E[t][r];
+        ET[seg & 1][j][row_of(t, r)] = E[t][r];
       }
   };
   auto doc_state = [&](int d) -> const float * {
     return S0 ? S0 + ((int64_t)d * H + h) * (D * D) : nullptr;
   };
+  // operands of the step producing E_s from segment s - 1's pair
+  auto load_ops = [&](int s, ScanOps &o) {
+    const float *P = pairs + ((int64_t)(s - 1) * H + h) * (D * 2 * D);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o.st[t][r] = P[row_of(t, r) * (2 * D) + col];  // S~
+      const float *Mrow = P + (32 * w + 16 * t + j) * (2 * D) + D;             // row of M
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        o.m[t][kb][0] = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g);
+        o.m[t][kb][1] = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g + 4);
+      }
+    }
+  };
+  // E_s = M E_{s-1} + S~ (E_{s-1} read from ET[(s - 1) & 1])
+  auto step = [&](int s, const ScanOps &o, floatx4 (&E)[2]) {
+    const int pb = (s - 1) & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc = o.st[t];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 a0 = o.m[t][kb][0], a1 = o.m[t][kb][1];
+        const float4 b0 = *reinterpret_cast<const float4 *>(&ET[pb][j][32 * kb + 8 * g]);
+        const float4 b1 = *reinterpret_cast<const float4 *>(&ET[pb][j][32 * kb + 8 * g + 4]);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        if constexpr (F32C) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(av[e], bv[e], acc);
+        } else {
+          bf16x8 ah, al, bh, bl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ah[e] = (__bf16)av[e];
+            al[e] = (__bf16)(av[e] - (float)ah[e]);
+            bh[e] = (__bf16)bv[e];
+            bl[e] = (__bf16)(bv[e] - (float)bh[e]);
+          }
+          acc = mfma_bf16_k32(al, bh, acc);
+          acc = mfma_bf16_k32(ah, bl, acc);
+          acc = mfma_bf16_k32(ah, bh, acc);
+        }
+      }
+      E[t] = acc;
+    }
+  };
 
   floatx4 E[2];
   load_state(doc_state(scan_doc_of(cu, N, 0)), E);
   publish(0, E);
+  ScanOps ops[2];
+  if (n_seg > 1) load_ops(1, ops[1]);
   __syncthreads();
 
-  for (int s = 1; s < n_seg; ++s) {
+  // Segment s's entry state from the previous one; the operands of step s + 1
+  // load while step s computes (two register sets, alternating).  One barrier
+  // per step: E_s is written to the other LDS buffer than E_{s-1}.
+  auto body = [&](int s, ScanOps &cur, ScanOps &nxt) {
+    if (s + 1 < n_seg) load_ops(s + 1, nxt);
     const int64_t pos = (int64_t)s * seg_len;
     const int d = scan_doc_of(cu, N, pos);
     const bool reset = cu ? ((int64_t)cu[d] == pos) : false;
     if (reset) {
       load_state(doc_state(d), E);
     } else {
-      const float *P = pairs + ((int64_t)(s - 1) * H + h) * (D * 2 * D);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        floatx4 acc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = P[row_of(t, r) * (2 * D) + col];  // S~
-        const float *Mrow = P + (32 * w + 16 * t + j) * (2 * D) + D;        // row of M
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const float4 a0 = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g);
-          const float4 a1 = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g + 4);
-          const float4 b0 = *reinterpret_cast<const float4 *>(&ET[j][32 * kb + 8 * g]);
-          const float4 b1 = *reinterpret_cast<const float4 *>(&ET[j][32 * kb + 8 * g + 4]);
-          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-          if constexpr (F32C) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(av[e], bv[e], acc);
-          } else {
-            bf16x8 ah, al, bh, bl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              ah[e] = (__bf16)av[e];
-              al[e] = (__bf16)(av[e] - (float)ah[e]);
-              bh[e] = (__bf16)bv[e];
-              bl[e] = (__bf16)(bv[e] - (float)bh[e]);
-            }
-            acc = mfma_bf16_k32(al, bh, acc);
-            acc = mfma_bf16_k32(ah, bl, acc);
-            acc = mfma_bf16_k32(ah, bh, acc);
-          }
-        }
-        E[t] = acc;
-      }
+      step(s, cur, E);
     }
-    __syncthreads();  // every wave has read the previous E slice
     publish(s, E);
     __syncthreads();
+  };
+  int s = 1;
+  for (; s + 1 < n_seg; s += 2) {
+    body(s, ops[1], ops[0]);
+    body(s + 1, ops[0], ops[1]);
   }
+  if (s < n_seg) body(s, ops[1], ops[0]);
 }
 
 hipError_t launch_pair_scan(const float *pairs, const float *S0, const int32_t *cu, int N,

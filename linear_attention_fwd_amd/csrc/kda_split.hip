@@ -49,6 +49,9 @@ struct __align__(16) ChunkImage {
 constexpr int IMG_BYTES = (int)sizeof(ChunkImage);
 constexpr int IMG_BLOCKS = IMG_BYTES / 1024;
 static_assert(IMG_BYTES % 1024 == 0, "chunk image must be whole 1 KB blocks");
+static_assert(offsetof(ChunkImage, Qd) % 1024 == 0 && offsetof(ChunkImage, KrT) % 1024 == 0 &&
+                  offsetof(ChunkImage, Mqk) % 1024 == 0 && offsetof(ChunkImage, INVb) % 1024 == 0,
+              "operand tiles must start on copy-block boundaries");
 constexpr int OFF_KD = (int)offsetof(ChunkImage, Kd);
 constexpr int OFF_QD = (int)offsetof(ChunkImage, Qd);
 constexpr int OFF_KRT = (int)offsetof(ChunkImage, KrT);
@@ -228,13 +231,14 @@ __device__ __forceinline__ bf16x8 pack_tiles(floatx4 t0, floatx4 t1) {
 //   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
 //   S <- Diag(gamma^C) S + K_restore^T U.
 // Each phase reads its MFMA A-operand fragments in one batch (lane (g, j): row
-// 16m + j, k elements 32kb + 8g .. +7).
+// 16m + j, k elements 32kb + 8g .. +7).  with_o = false skips O (segment
+// pairs, whose images are copied without Q_decay and M_qk).
 // O rows go through the bounded descriptor ro (tokens past the chunk are
 // dropped) at byte offset off_o + token * rowb, off_o = (j * H * D + first
 // column of the lane) * 2.
 __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], const floatx4 (&Vt)[4],
-                                         __amdgpu_buffer_rsrc_t ro, int off_o, int rowb, int g,
-                                         int j) {
+                                         bool with_o, __amdgpu_buffer_rsrc_t ro, int off_o, int rowb,
+                                         int g, int j) {
   using TD = Tile<bf16_t, D>;
   using TC = Tile<bf16_t, CH>;
   using PL = PackedLower;
@@ -284,7 +288,7 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], 
   // product swapped, lane (g, j) ends up with token 16m + j, columns 4g..4g+3
   // of this wave's slice and stores them with one 8-byte write.  Its stores
   // then complete while the state update runs.
-  {
+  if (with_o) {
     bf16x8 qd[4][4], mqk[6];
     int x = 0;
 #pragma unroll
@@ -411,6 +415,9 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
       const int bytes = (in_range && !m_cols && c.len > 0) ? ((c.len - 1) * H * D + SLICE) * ES : 0;
       return rsrc_words(v + (c.cs * H + h) * D + (split & 1) * SLICE, bytes);
     };
+    // Pairs produce no O: Q_decay and M_qk are not copied.
+    const bool pairs_only = p.rmode == 2;
+    auto in_blocks = [](int blk, int lo, int hi) { return blk >= lo / 1024 && blk < hi / 1024; };
     // chunk of slot sl -> buffer kk & 1: v in 1 KB blocks of 8 token rows
     // (blocks cw and cw + 4), the image in 1 KB blocks cw, cw + 4, ...
     auto issue_copy = [&](int64_t sl, int kk) {
@@ -424,7 +431,9 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
       }
       const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, IMG_BYTES);
       const uint32_t dst = lds_img + (uint32_t)((kk & 1) * IMG_BYTES);
-      for (int blk = cw; blk < IMG_BLOCKS; blk += 4) copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
+      for (int blk = cw; blk < IMG_BLOCKS; blk += 4)
+        if (!(pairs_only && (in_blocks(blk, OFF_QD, OFF_KRT) || in_blocks(blk, OFF_MQK, OFF_INVB))))
+          copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
     };
     // L2 prefetch of slot sl: this slice's half of the image and its v rows,
     // one dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
@@ -500,7 +509,7 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
       for (int r = 0; r < 4; ++r) Vt[m][r] = bf16_to_f32(vb[(16 * m + 4 * g + r) * SLICE + 16 * w + j]);
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(o + (c.cs * H + h) * D, p.rmode != 2 ? ((c.len - 1) * H + 1) * D * ES : 0);
-    rec_step(sm.buf[kk & 1], S, Vt, ro, off_o, rowb, g, j);
+    rec_step(sm.buf[kk & 1], S, Vt, p.rmode != 2, ro, off_o, rowb, g, j);
     if (c.last && p.rmode != 2 && p.final_state)
       state_store(S, uniptr(p.final_state + ((int64_t)c.d * H + h) * (D * D)), D, colW, g, j);
     sl = nsl;
