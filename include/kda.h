@@ -144,7 +144,10 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
  *   A. each (segment, head) computes its affine pair (M, S~) from a zero state
  *      (M = product of the per-token transitions; M = 0 when a document starts
  *      inside the segment, whose S~ then starts from that document's state);
- *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j;
+ *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j (on the
+ *      bf16 path in three levels: groups of about sqrt(n_segments) pairs are
+ *      composed into one pair each, the group pairs are scanned, and every
+ *      group is expanded from its entry state);
  *   C. every segment is re-run from its exact entry state, producing O and the
  *      final state of every document.
  * With bf16 arithmetic (dtype KDA_BF16, compute AUTO) the segments are equal

@@ -125,9 +125,23 @@ SegPlan plan_segments(int64_t units, int64_t requested) {
   const int64_t len = (units + n - 1) / n;
   return SegPlan{(units + len - 1) / len, len};
 }
+// The two-kernel path scans its segment pairs in three levels: groups of about
+// sqrt(n_seg) consecutive pairs are composed into one pair each (in parallel),
+// the group pairs are scanned, and each group is expanded from its entry state.
+// The dependent chain is about 3 sqrt(n_seg) pair applications instead of n_seg.
+int64_t scan_group_len(int64_t n_seg) {
+  int64_t g = 1;
+  while (g * g < n_seg) ++g;
+  return g;
+}
+int64_t scan_groups(int64_t n_seg) {
+  const int64_t g = scan_group_len(n_seg);
+  return (n_seg + g - 1) / g;
+}
 size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
   const SegPlan sp = plan_segments(kda::n_chunk_slots(T, N), requested);
-  return kda::split_workspace_bytes(T, N, H) + scan_workspace(sp.n_seg, H);
+  return kda::split_workspace_bytes(T, N, H) + scan_workspace(sp.n_seg, H) +
+         scan_workspace(scan_groups(sp.n_seg), H);
 }
 
 }  // namespace
@@ -296,6 +310,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     float *pairs = (float *)((char *)workspace + kda::split_workspace_bytes(T, N, H));
     float *entry = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
+    const int64_t glen = scan_group_len(sp.n_seg), n_groups = scan_groups(sp.n_seg);
+    float *gpairs = entry + (size_t)sp.n_seg * H * kD * kD;
+    float *gentry = gpairs + (size_t)n_groups * H * kD * 2 * kD;
 
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
                                       cu_seqlens, N, T, H, o, final_state, workspace);
@@ -309,8 +326,34 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states E_0 = 0, E_{j+1} = M_j E_j + S~_j (the first chunk is a
-    // document start, so E_0 never matters)
-    e = kda::launch_pair_scan(pairs, nullptr, nullptr, 1, T, H, (int)sp.n_seg, 0, entry, false, st);
+    // document start, so E_0 never matters), in three levels
+    kda::ScanChains sc{};
+    sc.pairs = pairs;
+    sc.H = H;
+    sc.n_pairs = (int)sp.n_seg;
+    sc.chain_len = (int)glen;
+    sc.n_chains = (int)n_groups;
+    sc.ncols = 2 * kD;
+    sc.mode = 1;  // B1: compose each group of pairs
+    sc.composed = gpairs;
+    e = kda::launch_scan_chains(sc, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group pairs");
+    sc.pairs = gpairs;  // B2: entry state of each group
+    sc.n_pairs = (int)n_groups;
+    sc.chain_len = (int)n_groups;
+    sc.n_chains = 1;
+    sc.ncols = kD;
+    sc.mode = 0;
+    sc.states = gentry;
+    e = kda::launch_scan_chains(sc, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group scan");
+    sc.pairs = pairs;  // B3: expand every group from its entry state
+    sc.n_pairs = (int)sp.n_seg;
+    sc.chain_len = (int)glen;
+    sc.n_chains = (int)n_groups;
+    sc.init = gentry;
+    sc.states = entry;
+    e = kda::launch_scan_chains(sc, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
     p.rmode = 1;  // C: re-run every segment from its exact entry state
     e = kda::launch_chunk_recurrence(p, st);
@@ -337,8 +380,8 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     hipError_t e = kda::launch_fwd(p, bf16_in, f32c, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states
-    e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, T, H, (int)sp.n_seg, sp.len,
-                              entry, f32c, st);
+    e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, H, (int)sp.n_seg, sp.len,
+                              entry, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
     // C: re-run every segment from its exact entry state
     p.mode = 1; p.item_init = entry; p.o = o; p.final_state = final_state;

@@ -74,8 +74,24 @@ hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);
 hipError_t launch_copy_empty(const int32_t *cu, int64_t T, const float *init, float *fin, int N,
                              int H, hipStream_t stream);
 hipError_t launch_pair_scan(const float *pairs, const float *S0, const int32_t *cu, int N,
-                            int64_t T, int H, int n_seg, int64_t seg_len, float *entry,
-                            bool f32_compute, hipStream_t stream);
+                            int H, int n_seg, int64_t seg_len, float *entry, hipStream_t stream);
+
+// Chains of segment-pair applications (a scan of pairs in levels); see
+// kda_scan_chains_kernel.  Pairs are [n_pairs, H, D, 2D] (columns 0..127 S~,
+// 128..255 M); chain c covers pairs [c * chain_len, min((c + 1) * chain_len, n_pairs)).
+struct ScanChains {
+  const float *pairs;
+  int H;
+  int n_pairs;
+  int chain_len;
+  int n_chains;
+  int ncols;          // 128 (states) or 256 (compose)
+  int mode;           // 0: write the state before each pair to states[i]; 1: compose
+  const float *init;  // mode 0: [n_chains, H, D, D] chain start states, or nullptr (0)
+  float *states;      // mode 0: [n_pairs, H, D, D]
+  float *composed;    // mode 1: [n_chains, H, D, 2D]
+};
+hipError_t launch_scan_chains(const ScanChains &sc, hipStream_t stream);
 
 template <typename Tin>
 hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, const void *ck,

@@ -12,16 +12,35 @@
 // 32 rows of E; the current E slice is shared through LDS (transposed so a
 // lane's B operand is one contiguous read, double-buffered so one barrier per
 // step suffices).  The scan is serial over segments, so each step's pair is
-// loaded during the previous step.  With bf16 arithmetic the product
-// uses a hi/lo split of both operands (three MFMAs, about 16 mantissa bits),
-// since errors in M E would otherwise propagate along the whole scan; the fp32
-// verification build uses fp32 MFMA.
+// loaded during the previous step.  This one-level scan serves the fp32
+// arithmetic path (fp32 MFMA); the bf16 path scans its pairs in three levels
+// with kda_scan_chains_kernel below, whose products use a hi/lo bf16 split of
+// both operands (three MFMAs, about 16 mantissa bits), since errors in M E
+// would otherwise propagate along the whole scan.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
 constexpr int SCAN_THREADS = 256;
+
+// Workgroups are dispatched to the 8 XCDs round-robin by block index, and every
+// XCD has its own L2.  All column slices of one unit (a head, or a chain and
+// head) read the same M rows, so they are given block indices congruent mod 8:
+// block b serves slice (b / 8) % nslices of unit (b / (8 nslices)) * 8 + b % 8.
+// The grid is rounded up to whole groups of 8 units; blocks past the last unit
+// exit at once.
+struct ScanBlock {
+  int unit, slice;
+};
+__device__ __forceinline__ ScanBlock scan_block(int nslices) {
+  const int b = blockIdx.x;
+  const int q = b >> 3;
+  return ScanBlock{(q / nslices) * 8 + (b & 7), q % nslices};
+}
+inline unsigned scan_grid(int64_t units, int nslices) {
+  return (unsigned)((units + 7) / 8 * 8 * nslices);
+}
 
 __device__ __forceinline__ int scan_doc_of(const int32_t *cu, int N, int64_t pos) {
   if (!cu) return 0;
@@ -42,15 +61,16 @@ struct ScanOps {
   floatx4 st[2];
 };
 
-template <bool F32C>
 __global__ void __launch_bounds__(SCAN_THREADS, 1)
 kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ S0,
                      const int32_t *__restrict__ cu, int N, int H, int n_seg, int64_t seg_len,
                      float *__restrict__ entry) {
   __shared__ __align__(16) float ET[2][16][D];  // E slice, [buffer][column][row]
 
-  const int h = blockIdx.x / 8;
-  const int cs = blockIdx.x % 8;
+  const ScanBlock sb = scan_block(8);
+  if (sb.unit >= H) return;
+  const int h = sb.unit;
+  const int cs = sb.slice;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -106,22 +126,8 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
         const float4 b1 = *reinterpret_cast<const float4 *>(&ET[pb][j][32 * kb + 8 * g + 4]);
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        if constexpr (F32C) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(av[e], bv[e], acc);
-        } else {
-          bf16x8 ah, al, bh, bl;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ah[e] = (__bf16)av[e];
-            al[e] = (__bf16)(av[e] - (float)ah[e]);
-            bh[e] = (__bf16)bv[e];
-            bl[e] = (__bf16)(bv[e] - (float)bh[e]);
-          }
-          acc = mfma_bf16_k32(al, bh, acc);
-          acc = mfma_bf16_k32(ah, bl, acc);
-          acc = mfma_bf16_k32(ah, bh, acc);
-        }
+        for (int e = 0; e < 8; ++e) acc = mfma_f32_k4(av[e], bv[e], acc);
       }
       E[t] = acc;
     }
@@ -137,8 +143,10 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
   // Segment s's entry state from the previous one; the operands of step s + 1
   // load while step s computes (two register sets, alternating).  One barrier
   // per step: E_s is written to the other LDS buffer than E_{s-1}.
+  // (The prefetch is unconditional -- the last step reloads its own operands --
+  // so that the compiler's wait counts never have to cover a path without it.)
   auto body = [&](int s, ScanOps &cur, ScanOps &nxt) {
-    if (s + 1 < n_seg) load_ops(s + 1, nxt);
+    load_ops(min(s + 1, n_seg - 1), nxt);
     const int64_t pos = (int64_t)s * seg_len;
     const int d = scan_doc_of(cu, N, pos);
     const bool reset = cu ? ((int64_t)cu[d] == pos) : false;
@@ -148,7 +156,7 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
       step(s, cur, E);
     }
     publish(s, E);
-    __syncthreads();
+    lds_barrier();  // LDS only: the next step's operand loads stay in flight
   };
   int s = 1;
   for (; s + 1 < n_seg; s += 2) {
@@ -158,16 +166,150 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
   if (s < n_seg) body(s, ops[1], ops[0]);
 }
 
+// ---------------------------------------------------------------------------
+// Chains of pair applications, for a scan of segment pairs in levels.  A chain
+// walks pairs first..last (last exclusive) of the pair array and keeps a state
+// X with ncols columns:
+//   mode 0 (states): X starts from init[chain] (or 0) and the state before each
+//     pair, X_i, is written to states[i]; X <- M_i X + S~_i;
+//   mode 1 (compose): X = [S~ | M] of the first pair, then X <- M_i X + [S~_i | 0]
+//     for the others, i.e. the pairs composed into one; written to composed[chain].
+// One workgroup per (chain, head, 16-column slice of X); each of the 4 waves
+// owns 32 rows.  Same step as the pair scan: M rows as the A operand from the
+// pair array (the next step's loaded during the current one), X slice from LDS
+// (double-buffered), products in bf16 hi/lo halves (three MFMAs).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(SCAN_THREADS, 1) kda_scan_chains_kernel(ScanChains sc) {
+  __shared__ __align__(16) float XT[2][16][D];  // X slice, [buffer][column][row]
+
+  const int nslices = sc.ncols / 16;
+  const ScanBlock sb = scan_block(nslices);
+  if (sb.unit >= sc.n_chains * sc.H) return;
+  const int chain = sb.unit / sc.H;
+  const int h = sb.unit % sc.H;
+  const int csl = sb.slice;
+  const int first = chain * sc.chain_len;
+  const int last = min(first + sc.chain_len, sc.n_pairs);
+  if (first >= last) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int col = 16 * csl + j;  // column of X (S~ part below D, M part from D on)
+  const bool st_on = 16 * csl < D;
+
+  auto row_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * g + r; };
+  auto pair_at = [&](int i) { return sc.pairs + ((int64_t)i * sc.H + h) * (D * 2 * D); };
+  auto share = [&](int buf, const floatx4 (&X)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) XT[buf][j][row_of(t, r)] = X[t][r];
+  };
+  auto write_state = [&](float *dst, int ld, const floatx4 (&X)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[row_of(t, r) * ld + col] = X[t][r];
+  };
+  auto load_ops = [&](int i, ScanOps &o) {
+    const float *P = pair_at(i);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // S~ (zero for the M columns; a load either way)
+        const float v = P[row_of(t, r) * (2 * D) + (col & (D - 1))];
+        o.st[t][r] = st_on ? v : 0.f;
+      }
+      const float *Mrow = P + (32 * w + 16 * t + j) * (2 * D) + D;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        o.m[t][kb][0] = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g);
+        o.m[t][kb][1] = *reinterpret_cast<const float4 *>(Mrow + 32 * kb + 8 * g + 4);
+      }
+    }
+  };
+  auto apply = [&](int pb, const ScanOps &o, floatx4 (&X)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc = o.st[t];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 a0 = o.m[t][kb][0], a1 = o.m[t][kb][1];
+        const float4 b0 = *reinterpret_cast<const float4 *>(&XT[pb][j][32 * kb + 8 * g]);
+        const float4 b1 = *reinterpret_cast<const float4 *>(&XT[pb][j][32 * kb + 8 * g + 4]);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        bf16x8 ah, al, bh, bl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ah[e] = (__bf16)av[e];
+          al[e] = (__bf16)(av[e] - (float)ah[e]);
+          bh[e] = (__bf16)bv[e];
+          bl[e] = (__bf16)(bv[e] - (float)bh[e]);
+        }
+        acc = mfma_bf16_k32(al, bh, acc);
+        acc = mfma_bf16_k32(ah, bl, acc);
+        acc = mfma_bf16_k32(ah, bh, acc);
+      }
+      X[t] = acc;
+    }
+  };
+
+  floatx4 X[2];
+  int i0;  // first pair applied
+  if (sc.mode == 1) {
+    const float *P = pair_at(first);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[t][r] = P[row_of(t, r) * (2 * D) + col];
+    i0 = first + 1;
+  } else {
+    const float *src = sc.init ? sc.init + ((int64_t)chain * sc.H + h) * (D * D) : nullptr;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[t][r] = src ? src[row_of(t, r) * D + col] : 0.f;
+    i0 = first;
+  }
+  share(0, X);
+  ScanOps ops[2];
+  if (i0 < last) load_ops(i0, ops[0]);
+  __syncthreads();
+
+  // step n applies pair i0 + n, reading X from XT[n & 1] and sharing the result
+  // in XT[(n + 1) & 1]; one barrier per step
+  // (unconditional prefetch, as in the pair scan)
+  auto body = [&](int n, ScanOps &cur, ScanOps &nxt) {
+    const int i = i0 + n;
+    load_ops(min(i + 1, last - 1), nxt);
+    if (sc.mode == 0) write_state(sc.states + ((int64_t)i * sc.H + h) * (D * D), D, X);
+    apply(n & 1, cur, X);
+    share((n + 1) & 1, X);
+    lds_barrier();  // LDS only: the next step's operand loads stay in flight
+  };
+  const int nsteps = last - i0;
+  int n = 0;
+  for (; n + 1 < nsteps; n += 2) {
+    body(n, ops[0], ops[1]);
+    body(n + 1, ops[1], ops[0]);
+  }
+  if (n < nsteps) body(n, ops[0], ops[1]);
+  if (sc.mode == 1) write_state(sc.composed + ((int64_t)chain * sc.H + h) * (D * 2 * D), 2 * D, X);
+}
+
+hipError_t launch_scan_chains(const ScanChains &sc, hipStream_t stream) {
+  const dim3 grid(scan_grid((int64_t)sc.n_chains * sc.H, sc.ncols / 16));
+  hipLaunchKernelGGL(kda_scan_chains_kernel, grid, dim3(SCAN_THREADS), 0, stream, sc);
+  return hipGetLastError();
+}
+
 hipError_t launch_pair_scan(const float *pairs, const float *S0, const int32_t *cu, int N,
-                            int64_t /*T*/, int H, int n_seg, int64_t seg_len, float *entry,
-                            bool f32_compute, hipStream_t stream) {
-  const dim3 grid((unsigned)(H * 8));
-  if (f32_compute)
-    hipLaunchKernelGGL(kda_pair_scan_kernel<true>, grid, dim3(SCAN_THREADS), 0, stream, pairs,
-                       S0, cu, N, H, n_seg, seg_len, entry);
-  else
-    hipLaunchKernelGGL(kda_pair_scan_kernel<false>, grid, dim3(SCAN_THREADS), 0, stream, pairs,
-                       S0, cu, N, H, n_seg, seg_len, entry);
+                            int H, int n_seg, int64_t seg_len, float *entry, hipStream_t stream) {
+  hipLaunchKernelGGL(kda_pair_scan_kernel, dim3(scan_grid(H, 8)), dim3(SCAN_THREADS), 0, stream,
+                     pairs, S0, cu, N, H, n_seg, seg_len, entry);
   return hipGetLastError();
 }
 
