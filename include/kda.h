@@ -144,12 +144,14 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
  *   A. each (segment, head) computes its affine pair (M, S~) from a zero state
  *      (M = product of the per-token transitions; M = 0 when a document starts
  *      inside the segment, whose S~ then starts from that document's state);
- *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j (on the
- *      bf16 path in three levels: groups of about sqrt(n_segments) pairs are
- *      composed into one pair each, the group pairs are scanned, and every
- *      group is expanded from its entry state);
+ *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j;
  *   C. every segment is re-run from its exact entry state, producing O and the
  *      final state of every document.
+ * On the bf16 path, B and C work on groups of about sqrt(n_segments)
+ * consecutive segments: the pairs of a group are composed into one pair, the
+ * group pairs are scanned into the entry state of each group, and the segments
+ * of a group are re-run back to back from it (each then starts from the state
+ * the previous one ends with, its exact entry state).
  * With bf16 arithmetic (dtype KDA_BF16, compute AUTO) the segments are equal
  * ranges of 64-token chunk slots (see kda_chunk_fwd_workspace_size) and all
  * three phases run on the two kernels of kda_chunk_fwd over one chunk prep;

@@ -125,10 +125,11 @@ SegPlan plan_segments(int64_t units, int64_t requested) {
   const int64_t len = (units + n - 1) / n;
   return SegPlan{(units + len - 1) / len, len};
 }
-// The two-kernel path scans its segment pairs in three levels: groups of about
-// sqrt(n_seg) consecutive pairs are composed into one pair each (in parallel),
-// the group pairs are scanned, and each group is expanded from its entry state.
-// The dependent chain is about 3 sqrt(n_seg) pair applications instead of n_seg.
+// The two-kernel path scans its segment pairs in two levels: groups of about
+// sqrt(n_seg) consecutive pairs are composed into one pair each (in parallel)
+// and the group pairs are scanned into the entry state of each group; the
+// re-run then walks each group's segments back to back from that state.  The
+// dependent chain is about 2 sqrt(n_seg) pair applications instead of n_seg.
 int64_t scan_group_len(int64_t n_seg) {
   int64_t g = 1;
   while (g * g < n_seg) ++g;
@@ -140,7 +141,8 @@ int64_t scan_groups(int64_t n_seg) {
 }
 size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
   const SegPlan sp = plan_segments(kda::n_chunk_slots(T, N), requested);
-  return kda::split_workspace_bytes(T, N, H) + scan_workspace(sp.n_seg, H) +
+  // chunk images, segment pairs [., D, 2D], group pairs and group entry states
+  return kda::split_workspace_bytes(T, N, H) + (size_t)sp.n_seg * H * kD * 2 * kD * sizeof(float) +
          scan_workspace(scan_groups(sp.n_seg), H);
 }
 
@@ -309,16 +311,14 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     float *pairs = (float *)((char *)workspace + kda::split_workspace_bytes(T, N, H));
-    float *entry = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
     const int64_t glen = scan_group_len(sp.n_seg), n_groups = scan_groups(sp.n_seg);
-    float *gpairs = entry + (size_t)sp.n_seg * H * kD * kD;
+    float *gpairs = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
     float *gentry = gpairs + (size_t)n_groups * H * kD * 2 * kD;
 
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
                                       cu_seqlens, N, T, H, o, final_state, workspace);
     p.n_seg = (int)sp.n_seg;
     p.seg_slots = sp.len;
-    p.entry = entry;
     p.pairs = pairs;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan prep");
@@ -326,7 +326,11 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states E_0 = 0, E_{j+1} = M_j E_j + S~_j (the first chunk is a
-    // document start, so E_0 never matters), in three levels
+    // document start, so E_0 never matters), for the first segment of each
+    // group of glen segments: the pairs of a group are composed into one, and
+    // the group pairs are scanned
+    const int n_cu = kda_default_segments();  // compute units, or an error status
+    if (n_cu < 0) return n_cu;
     kda::ScanChains sc{};
     sc.pairs = pairs;
     sc.H = H;
@@ -336,7 +340,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     sc.ncols = 2 * kD;
     sc.mode = 1;  // B1: compose each group of pairs
     sc.composed = gpairs;
-    e = kda::launch_scan_chains(sc, st);
+    e = kda::launch_scan_chains(sc, n_cu, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group pairs");
     sc.pairs = gpairs;  // B2: entry state of each group
     sc.n_pairs = (int)n_groups;
@@ -345,17 +349,15 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     sc.ncols = kD;
     sc.mode = 0;
     sc.states = gentry;
-    e = kda::launch_scan_chains(sc, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group scan");
-    sc.pairs = pairs;  // B3: expand every group from its entry state
-    sc.n_pairs = (int)sp.n_seg;
-    sc.chain_len = (int)glen;
-    sc.n_chains = (int)n_groups;
-    sc.init = gentry;
-    sc.states = entry;
-    e = kda::launch_scan_chains(sc, st);
+    e = kda::launch_scan_chains(sc, n_cu, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
-    p.rmode = 1;  // C: re-run every segment from its exact entry state
+    // C: re-run the segments of each group back to back from the group's entry
+    // state; each one then starts from the state the previous one ends with,
+    // which is its exact entry state
+    p.rmode = 1;
+    p.n_seg = (int)n_groups;
+    p.seg_slots = glen * sp.len;
+    p.entry = gentry;
     e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
   } else if (T > 0) {

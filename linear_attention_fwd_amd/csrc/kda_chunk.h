@@ -167,9 +167,16 @@ template <> struct Arith<true> {  // fp32 operands, fp32 MFMA
 };
 
 // ---- document and chunk bookkeeping ----------------------------------------
+// The document offsets are read through the constant address space, so that
+// with a uniform index they come in by scalar loads.  Vector loads would share
+// the wave's vmcnt with its copies and stores, and waiting for one of them
+// would wait for all of those issued before it.
+__device__ __forceinline__ int64_t cu_load(const int32_t *cu, int i) {
+  return (int64_t)((const __attribute__((address_space(4))) int32_t *)cu)[i];
+}
 // document offsets; cu == nullptr means one document [0, T)
 __device__ __forceinline__ int64_t cu_at(const int32_t *cu, int64_t T, int i) {
-  return cu ? (int64_t)cu[i] : (i == 0 ? (int64_t)0 : T);
+  return cu ? cu_load(cu, i) : (i == 0 ? (int64_t)0 : T);
 }
 // largest d in [0, N-1] with cu[d] <= pos (skips empty documents starting at pos)
 __device__ __forceinline__ int doc_of(const int32_t *cu, int N, int64_t pos) {
@@ -177,7 +184,7 @@ __device__ __forceinline__ int doc_of(const int32_t *cu, int N, int64_t pos) {
   int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)cu[mid] <= pos) lo = mid; else hi = mid - 1;
+    if (cu_load(cu, mid) <= pos) lo = mid; else hi = mid - 1;
   }
   return uni(lo);
 }
@@ -187,7 +194,7 @@ __device__ __forceinline__ int doc_of_slot(const int32_t *cu, int N, int64_t slo
   int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (first_slot(cu[mid], mid) <= slot) lo = mid; else hi = mid - 1;
+    if (first_slot(cu_load(cu, mid), mid) <= slot) lo = mid; else hi = mid - 1;
   }
   return uni(lo);
 }

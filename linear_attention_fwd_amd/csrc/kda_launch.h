@@ -91,7 +91,8 @@ struct ScanChains {
   float *states;      // mode 0: [n_pairs, H, D, D]
   float *composed;    // mode 1: [n_chains, H, D, 2D]
 };
-hipError_t launch_scan_chains(const ScanChains &sc, hipStream_t stream);
+// n_cu: compute units of the device (chooses the columns per workgroup)
+hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream);
 
 template <typename Tin>
 hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, const void *ck,

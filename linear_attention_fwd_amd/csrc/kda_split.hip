@@ -201,23 +201,31 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitPar
 }
 
 // ---------------------------------------------------------------------------
-// Recurrence: two workgroups per (document, head), each owning 64 state
-// columns; the two share an XCD (blockIdx % 8), so the second copy of a chunk
-// image comes from L2.  A workgroup has 8 waves: waves 0..3 compute (16
-// columns each), waves 4..7 only copy the next chunk's image and v rows into
-// the LDS double buffer and pull later chunks into L2.  A wave stalls while
-// its copies queue up; with the roles split, those stalls fall on the copy
-// wave of each SIMD while the compute wave keeps its MFMA work going.
+// Recurrence: one workgroup per (item, head, column slice).  A workgroup has 8
+// waves: waves 0..3 compute, waves 4..7 only copy the next chunk's image and v
+// rows into the LDS double buffer and pull later chunks into L2.  A wave
+// stalls while its copies queue up; with the roles split, those stalls fall on
+// the copy wave of each SIMD while the compute wave keeps its MFMA work going.
+//
+// A compute wave owns NT tiles of 16 state columns, so a workgroup owns 64 NT
+// columns.  Every workgroup copies the whole image of each chunk, whatever its
+// column count, and that copy bounds the time per chunk; so where there are
+// fewer (item, head) units than compute units, NT = 1 spreads each unit over
+// two workgroups (four for segment pairs, whose state is 256 columns wide),
+// and where there are more, NT = 2 halves the number of chunk steps.  The
+// workgroups of one unit share an XCD (blockIdx % 8), so the image reaches
+// them from one L2.
 // ---------------------------------------------------------------------------
 constexpr int REC_THREADS = 512;
 constexpr int REC_COMPUTE_WAVES = 4;
 constexpr int REC_COPY_THREADS = REC_THREADS - 64 * REC_COMPUTE_WAVES;
-constexpr int SLICE = 64;  // state columns per workgroup
-struct __align__(16) RecSmem {
+template <int NT> struct __align__(16) RecSmem {
+  static constexpr int SLICE = 64 * NT;  // state columns per workgroup
   ChunkImage buf[2];
-  bf16_t V[2][CH * SLICE];  // v rows of the chunk, this workgroup's columns (128 B per token)
+  bf16_t V[2][CH * SLICE];  // v rows of the chunk, this workgroup's columns
   uint32_t sink[64];        // destination of the L2 prefetch touches; never read
 };
+static_assert(sizeof(RecSmem<2>) <= 160 * 1024, "recurrence LDS exceeds a compute unit");
 
 __device__ __forceinline__ bf16x8 frag(const bf16_t *tile, int idx) {
   return *reinterpret_cast<const bf16x8 *>(tile + idx);
@@ -226,40 +234,55 @@ __device__ __forceinline__ bf16x8 pack_tiles(floatx4 t0, floatx4 t1) {
   return to_bf16x8(floatx8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]});
 }
 
-// The chunk recurrence (chunk_recurrence in kda_chunk.h) for this wave's 16
-// state columns, operands from the chunk image in LDS:
+// The chunk recurrence (chunk_recurrence in kda_chunk.h) for this wave's NT
+// tiles of 16 state columns, operands from the chunk image in LDS:
 //   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
 //   S <- Diag(gamma^C) S + K_restore^T U.
 // Each phase reads its MFMA A-operand fragments in one batch (lane (g, j): row
-// 16m + j, k elements 32kb + 8g .. +7).  with_o = false skips O (segment
-// pairs, whose images are copied without Q_decay and M_qk).
+// 16m + j, k elements 32kb + 8g .. +7) and applies them to every tile.
+// with_o = false skips O (segment pairs, whose images are copied without
+// Q_decay and M_qk).  V: the v rows of the chunk in LDS (vld elements per row),
+// tile t of this wave at column vcol + 16 t.
 // O rows go through the bounded descriptor ro (tokens past the chunk are
-// dropped) at byte offset off_o + token * rowb, off_o = (j * H * D + first
-// column of the lane) * 2.
-__device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], const floatx4 (&Vt)[4],
-                                         bool with_o, __amdgpu_buffer_rsrc_t ro, int off_o, int rowb,
-                                         int g, int j) {
+// dropped) at byte offset off_o + token * rowb + 32 t, off_o = (j * H * D +
+// first column of the lane) * 2.
+template <int NT>
+__device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][8], const bf16_t *V,
+                                         int vld, int vcol, bool with_o, __amdgpu_buffer_rsrc_t ro,
+                                         int off_o, int rowb, int g, int j) {
   using TD = Tile<bf16_t, D>;
   using TC = Tile<bf16_t, CH>;
   using PL = PackedLower;
-  bf16x8 sb[4];
+  // fragments read per batch: the whole phase for one tile; one 16-row block
+  // at a time for two (each fragment then feeds twice the MFMA work, and the
+  // whole-phase batches would not fit the register budget)
+  constexpr int MB = NT == 1 ? 4 : 1;
+  bf16x8 sb[NT][4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) sb[kb] = pack_tiles(S[2 * kb], S[2 * kb + 1]);
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sb[t][kb] = pack_tiles(S[t][2 * kb], S[t][2 * kb + 1]);
   // U' = V - K_decay S
-  floatx4 U[4];
-  {
-    bf16x8 kd[4][4];
+  floatx4 U[NT][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+  for (int m0 = 0; m0 < 4; m0 += MB) {
+    bf16x8 kd[MB][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kd[m][kb] = frag(im.Kd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+    for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) kd[mm][kb] = frag(im.Kd, TD::idx(16 * (m0 + mm) + j, 32 * kb + 8 * g));
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(kd[m][kb], sb[kb], x);
-      U[m] = Vt[m] - x;
-    }
+    for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int m = m0 + mm;
+        floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(kd[mm][kb], sb[t][kb], x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          U[t][m][r] = bf16_to_f32(V[(16 * m + 4 * g + r) * vld + vcol + 16 * t + j]) - x[r];
+      }
   }
   // U = INV Diag(beta) U'
   {
@@ -269,65 +292,79 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[8], 
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int kb = 0; kb <= (m >> 1); ++kb, ++x) inv[x] = frag(im.INVb, PL::idx(16 * m + j, 32 * kb + 8 * g));
-    bf16x8 bb[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
-    x = 0;
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 bb[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[t][2 * kb], U[t][2 * kb + 1]);
+      x = 0;
 #pragma unroll
-      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(inv[x], bb[kb], acc);
-      U[m] = acc;
+      for (int m = 0; m < 4; ++m) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(inv[x], bb[kb], acc);
+        U[t][m] = acc;
+      }
     }
   }
-  bf16x8 ub[2];
+  bf16x8 ub[NT][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) ub[kb] = pack_tiles(U[2 * kb], U[2 * kb + 1]);
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) ub[t][kb] = pack_tiles(U[t][2 * kb], U[t][2 * kb + 1]);
   // O = Q_decay S + M_qk U, formed transposed: with the operands of each
   // product swapped, lane (g, j) ends up with token 16m + j, columns 4g..4g+3
-  // of this wave's slice and stores them with one 8-byte write.  Its stores
-  // then complete while the state update runs.
+  // of the tile and stores them with one 8-byte write.  Its stores then
+  // complete while the state update runs.
   if (with_o) {
-    bf16x8 qd[4][4], mqk[6];
-    int x = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m0 = 0; m0 < 4; m0 += MB) {
+      bf16x8 qd[MB][4], mqk[MB][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) qd[m][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+      for (int mm = 0; mm < MB; ++mm) {
+        const int m = m0 + mm;
 #pragma unroll
-      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) mqk[x] = frag(im.Mqk, PL::idx(16 * m + j, 32 * kb + 8 * g));
-    }
-    x = 0;
+        for (int kb = 0; kb < 4; ++kb) qd[mm][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb <= (m >> 1); ++kb) mqk[mm][kb] = frag(im.Mqk, PL::idx(16 * m + j, 32 * kb + 8 * g));
+      }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(sb[kb], qd[m][kb], acc);
+      for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
-      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(ub[kb], mqk[x], acc);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(acc)), ro,
-                                            off_o + (16 * m) * rowb, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          const int m = m0 + mm;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(sb[t][kb], qd[mm][kb], acc);
+#pragma unroll
+          for (int kb = 0; kb <= (m >> 1); ++kb) acc = mfma_bf16_k32(ub[t][kb], mqk[mm][kb], acc);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(acc)), ro,
+                                                off_o + (16 * m) * rowb + 32 * t, 0, 0);
+        }
     }
   }
   // S <- Diag(gamma^C) S + K_restore^T U
-  {
-    bf16x8 krt[8][2];
-    float4 gam[8];
+  constexpr int MS = NT == 1 ? 8 : 2;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+  for (int m0 = 0; m0 < 8; m0 += MS) {
+    bf16x8 krt[MS][2];
+    float4 gam[MS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) krt[m][kb] = frag(im.KrT, TC::idx(16 * m + j, 32 * kb + 8 * g));
-      gam[m] = *reinterpret_cast<const float4 *>(&im.gamC[16 * m + 4 * g]);
+    for (int mm = 0; mm < MS; ++mm) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) krt[mm][kb] = frag(im.KrT, TC::idx(16 * (m0 + mm) + j, 32 * kb + 8 * g));
+      gam[mm] = *reinterpret_cast<const float4 *>(&im.gamC[16 * (m0 + mm) + 4 * g]);
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      floatx4 acc = S[m];
-      acc[0] *= gam[m].x; acc[1] *= gam[m].y; acc[2] *= gam[m].z; acc[3] *= gam[m].w;
+    for (int mm = 0; mm < MS; ++mm)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(krt[m][kb], ub[kb], acc);
-      S[m] = acc;
-    }
+      for (int t = 0; t < NT; ++t) {
+        floatx4 acc = S[t][m0 + mm];
+        acc[0] *= gam[mm].x; acc[1] *= gam[mm].y; acc[2] *= gam[mm].z; acc[3] *= gam[mm].w;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(krt[mm][kb], ub[t][kb], acc);
+        S[t][m0 + mm] = acc;
+      }
   }
 }
 
@@ -356,20 +393,35 @@ __device__ __forceinline__ int64_t next_chunk_slot(const SplitParams &p, int64_t
   return s;
 }
 
-// One workgroup per (item, head, 64-column slice).  Items: documents (rmode 0),
-// or segments of seg_slots chunk slots (rmode 1: re-run from the segment's
-// entry state, writing O and the final states of documents ending inside;
-// rmode 2: the segment's pair, state [S~ | M] from [0 | I] with v = 0 on the
-// M columns, four slices).  At the first chunk of a document the state is
-// reset to that document's initial state (M columns: 0), so a pair whose
-// segment contains a document start has M = 0 and the scan needs no document
-// logic.
-__global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
-  using IO = bufio<bf16_t>;
-  constexpr int ES = 2;
-  __shared__ RecSmem sm;
+// Parts of the image the L2 touches cover, in 64-byte lines: all operands, or
+// for segment pairs only K_decay, K_restore^T, INV Diag(beta) and gamma^C.
+constexpr int IMG_LINES_ALL = (OFF_GAMC + 4 * D) / 64;
+constexpr int KD_LINES = (OFF_QD - OFF_KD) / 64;
+constexpr int KRT_LINES = (OFF_MQK - OFF_KRT) / 64;
+constexpr int IMG_LINES_PAIRS = KD_LINES + KRT_LINES + (OFF_GAMC + 4 * D - OFF_INVB) / 64;
+static_assert(OFF_KD == 0 && OFF_GAMC == OFF_INVB + 2 * PackedLower::ELEMS, "image layout");
+__device__ __forceinline__ int touch_line_offset(int line, bool pairs_only) {
+  if (!pairs_only) return 64 * line;
+  if (line < KD_LINES) return 64 * line;
+  if (line < KD_LINES + KRT_LINES) return OFF_KRT + 64 * (line - KD_LINES);
+  return OFF_INVB + 64 * (line - KD_LINES - KRT_LINES);
+}
 
-  const int nsplit = p.rmode == 2 ? 4 : 2;
+// Items: documents (rmode 0), or segments of seg_slots chunk slots (rmode 1:
+// re-run from the segment's entry state, writing O and the final states of
+// documents ending inside; rmode 2: the segment's pair, state [S~ | M] from
+// [0 | I] with v = 0 on the M columns).  At the first chunk of a document the
+// state is reset to that document's initial state (M columns: 0), so a pair
+// whose segment contains a document start has M = 0 and the scan needs no
+// document logic.
+template <int NT>
+__global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitParams p) {
+  using Smem = RecSmem<NT>;
+  constexpr int SLICE = Smem::SLICE;
+  constexpr int ES = 2;
+  __shared__ Smem sm;
+
+  const int nsplit = (p.rmode == 2 ? 4 : 2) / NT;
   const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
   const int xlo = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
@@ -391,7 +443,8 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   }
   s_begin = uni64(s_begin);
   s_end = uni64(s_end);
-  const bool m_cols = p.rmode == 2 && split >= 2;  // M columns of a pair: v = 0, start from I
+  const int col0 = split * SLICE;            // first state column of the workgroup
+  const bool m_cols = col0 >= D;             // M columns of a pair: v = 0, start from I
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,21 +466,26 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
     // of them for M columns or past the range) read 0
     auto v_rsrc = [&](const SlotChunk &c, bool in_range) {
       const int bytes = (in_range && !m_cols && c.len > 0) ? ((c.len - 1) * H * D + SLICE) * ES : 0;
-      return rsrc_words(v + (c.cs * H + h) * D + (split & 1) * SLICE, bytes);
+      return rsrc_words(v + (c.cs * H + h) * D + col0 % D, bytes);
     };
     // Pairs produce no O: Q_decay and M_qk are not copied.
     const bool pairs_only = p.rmode == 2;
     auto in_blocks = [](int blk, int lo, int hi) { return blk >= lo / 1024 && blk < hi / 1024; };
-    // chunk of slot sl -> buffer kk & 1: v in 1 KB blocks of 8 token rows
-    // (blocks cw and cw + 4), the image in 1 KB blocks cw, cw + 4, ...
+    // v rows in 1 KB blocks of VROWS token rows (LPR lanes per row)
+    constexpr int LPR = SLICE * ES / 16;
+    constexpr int VROWS = 64 / LPR;
+    constexpr int VBLOCKS = CH / VROWS;
+    static_assert(VBLOCKS % 4 == 0, "v blocks per copy wave");
+    // chunk of slot sl -> buffer kk & 1: v blocks cw, cw + 4, ..., the image in
+    // 1 KB blocks cw, cw + 4, ...
     auto issue_copy = [&](int64_t sl, int kk) {
       const SlotChunk c = slot_chunk(p, sl);
       const i32x4 rv = v_rsrc(c, true);
       const uint32_t vdst = lds_v + (uint32_t)((kk & 1) * CH * SLICE * ES);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < VBLOCKS / 4; ++i) {
         const int blk = cw + 4 * i;
-        copy16_to_lds(rv, vdst + blk * 1024, (8 * blk + (lane >> 3)) * rowb + (lane & 7) * 16);
+        copy16_to_lds(rv, vdst + blk * 1024, (VROWS * blk + lane / LPR) * rowb + (lane % LPR) * 16);
       }
       const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, IMG_BYTES);
       const uint32_t dst = lds_img + (uint32_t)((kk & 1) * IMG_BYTES);
@@ -435,24 +493,32 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
         if (!(pairs_only && (in_blocks(blk, OFF_QD, OFF_KRT) || in_blocks(blk, OFF_MQK, OFF_INVB))))
           copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
     };
-    // L2 prefetch of slot sl: this slice's half of the image and its v rows,
-    // one dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
+    // L2 prefetch of slot sl: this workgroup's share of the image lines its
+    // unit reads (one part per workgroup of the unit) and its v rows, one
+    // dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
     // (offsets past the data, or a slot past the range, fetch nothing), so the
     // wait at the top of the loop can leave exactly these in flight.
-    constexpr int TOUCH_OPS = 3;
+    constexpr int TOUCH_IMG = NT == 1 ? 2 : 4;
+    constexpr int TOUCH_OPS = TOUCH_IMG + 1;
     constexpr int OOB = 1 << 30;
-    constexpr int HALF = IMG_BYTES / 2;
-    static_assert(HALF / 64 <= 2 * REC_COPY_THREADS && 2 * CH <= REC_COPY_THREADS, "touch coverage");
+    constexpr int VLINES = SLICE * ES / 64;  // 64-byte lines per v row
+    static_assert(CH * VLINES <= REC_COPY_THREADS, "v touch coverage");
+    static_assert((IMG_LINES_ALL + 1) / 2 <= TOUCH_IMG * REC_COPY_THREADS || NT == 2, "touch coverage");
+    static_assert(IMG_LINES_ALL <= 4 * REC_COPY_THREADS, "touch coverage");
+    const int n_lines = pairs_only ? IMG_LINES_PAIRS : IMG_LINES_ALL;
+    const int part_lines = (n_lines + nsplit - 1) / nsplit;
     auto issue_touch = [&](int64_t sl) {
       const bool in_range = sl < s_end;
       const SlotChunk c = slot_chunk(p, in_range ? sl : s_begin);
       const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, in_range ? IMG_BYTES : 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int idx = i * REC_COPY_THREADS + ct;
-        touch4_to_lds(ri, lds_sink, idx < HALF / 64 ? (split & 1) * HALF + idx * 64 : OOB);
+      for (int i = 0; i < TOUCH_IMG; ++i) {
+        const int k = i * REC_COPY_THREADS + ct;
+        const int line = split * part_lines + k;
+        touch4_to_lds(ri, lds_sink, k < part_lines && line < n_lines ? touch_line_offset(line, pairs_only) : OOB);
       }
-      touch4_to_lds(v_rsrc(c, in_range), lds_sink, ct < 2 * CH ? (ct >> 1) * rowb + (ct & 1) * 64 : OOB);
+      touch4_to_lds(v_rsrc(c, in_range), lds_sink,
+                    ct < CH * VLINES ? (ct / VLINES) * rowb + (ct % VLINES) * 64 : OOB);
     };
     constexpr int AHEAD = 2;  // slots between a touch and the copy that uses it
 
@@ -476,18 +542,25 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   // ---------------- compute waves ----------------
   const int g = lane >> 4;
   const int j = lane & 15;
-  const int colW = split * SLICE + 16 * w;
-  floatx4 S[8];
+  const int vcol = 16 * NT * w;  // first column of this wave within the slice
+  const int colW = col0 + vcol;  // first state column of tile 0
+  floatx4 S[NT][8];
   if (p.rmode == 1) {
-    state_load(S, uniptr(p.entry + ((int64_t)item * H + h) * (D * D)), D, colW, g, j);
+    const float *e = uniptr(p.entry + ((int64_t)item * H + h) * (D * D));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) state_load(S[t], e, D, colW + 16 * t, g, j);
+    wait_vmem();  // before the loop: a wait inside it would also cover the O stores
   } else {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[m][r] = (m_cols && 16 * m + 4 * g + r == colW + j - D) ? 1.f : 0.f;
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[t][m][r] = (m_cols && 16 * m + 4 * g + r == colW + 16 * t + j - D) ? 1.f : 0.f;
   }
   bf16_t *o = (bf16_t *)p.o;
-  const int off_o = (j * H * D + colW + 4 * g) * ES;  // token j, columns 4g..4g+3
+  const int off_o = (j * H * D + colW + 4 * g) * ES;  // token j, columns 4g..4g+3 of tile 0
   int64_t sl = next_chunk_slot(p, s_begin, s_end);
   for (int kk = 0; sl < s_end; ++kk) {
     const int64_t nsl = next_chunk_slot(p, sl + 1, s_end);
@@ -495,27 +568,47 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
     lds_barrier();  // the copy of this chunk is complete in buffer kk & 1
     if (c.first) {  // a document starts: its initial state (M columns: 0)
       if (!m_cols && p.init) {
-        state_load(S, uniptr(p.init + ((int64_t)c.d * H + h) * (D * D)), D, colW, g, j);
+        const float *s0 = uniptr(p.init + ((int64_t)c.d * H + h) * (D * D));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) state_load(S[t], s0, D, colW + 16 * t, g, j);
+        // Wait for these loads here.  Left to the compiler, the wait falls
+        // where this branch rejoins the loop and, loads and stores completing
+        // in issue order, would hold every chunk until the previous chunk's O
+        // stores had reached memory.
+        wait_vmem();
       } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) S[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) S[t][m] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    floatx4 Vt[4];
-    const bf16_t *vb = &sm.V[kk & 1][0];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Vt[m][r] = bf16_to_f32(vb[(16 * m + 4 * g + r) * SLICE + 16 * w + j]);
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(o + (c.cs * H + h) * D, p.rmode != 2 ? ((c.len - 1) * H + 1) * D * ES : 0);
-    rec_step(sm.buf[kk & 1], S, Vt, p.rmode != 2, ro, off_o, rowb, g, j);
-    if (c.last && p.rmode != 2 && p.final_state)
-      state_store(S, uniptr(p.final_state + ((int64_t)c.d * H + h) * (D * D)), D, colW, g, j);
+    if constexpr (NT == 1) {
+      rec_step<NT>(sm.buf[kk & 1], S, &sm.V[kk & 1][0], SLICE, vcol, p.rmode != 2, ro, off_o, rowb, g, j);
+    } else {
+      // The per-lane operand addresses are cheap to form but would not all
+      // fit in registers across the loop: derive them anew in each chunk from
+      // a lane index the compiler cannot see through.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int gi = ln >> 4, ji = ln & 15;
+      rec_step<NT>(sm.buf[kk & 1], S, &sm.V[kk & 1][0], SLICE, vcol, p.rmode != 2, ro,
+                   (ji * H * D + colW + 4 * gi) * ES, rowb, gi, ji);
+    }
+    if (c.last && p.rmode != 2 && p.final_state) {
+      float *f = uniptr(p.final_state + ((int64_t)c.d * H + h) * (D * D));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) state_store(S[t], f, D, colW + 16 * t, g, j);
+    }
     sl = nsl;
   }
-  if (p.rmode == 2)  // the segment's pair [S~ | M]
-    state_store(S, uniptr(p.pairs + ((int64_t)item * H + h) * (D * 2 * D)), 2 * D, colW, g, j);
+  if (p.rmode == 2) {  // the segment's pair [S~ | M]
+    float *pr = uniptr(p.pairs + ((int64_t)item * H + h) * (D * 2 * D));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) state_store(S[t], pr, 2 * D, colW + 16 * t, g, j);
+  }
 }
 
 size_t split_workspace_bytes(int64_t T, int N, int H) {
@@ -528,14 +621,30 @@ hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// compute units of the current device (0 if unknown), cached per device
+static int device_cus() {
+  static int cached[64];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cached[dev] = cus;
+  return cus;
+}
+
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
-  // slices of one (item, head) share an XCD: two for documents and re-runs,
-  // four for pairs
+  // Two column tiles per compute wave once the (item, head) units alone fill
+  // the device; the workgroups of one unit share an XCD
   const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
+  const int cus = device_cus();
+  const bool wide = cus > 0 && units >= cus;
   const int groups = (units + 7) / 8;
-  const int nsplit = p.rmode == 2 ? 4 : 2;
-  hipLaunchKernelGGL(kda_chunk_rec_kernel, dim3((unsigned)(groups * 8 * nsplit)), dim3(REC_THREADS), 0,
-                     stream, p);
+  const int nsplit = (p.rmode == 2 ? 4 : 2) / (wide ? 2 : 1);
+  const dim3 grid((unsigned)(groups * 8 * nsplit));
+  if (wide)
+    hipLaunchKernelGGL(kda_chunk_rec_kernel<2>, grid, dim3(REC_THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kda_chunk_rec_kernel<1>, grid, dim3(REC_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 

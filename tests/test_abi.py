@@ -100,14 +100,14 @@ def test_prefill_validation(lib, fn):
 
 def test_segment_scan_workspace_checks(lib):
     # explicit segment count: a short or missing workspace is refused before any launch
-    # enough for either path: chunk images + pairs + entry states of the chunk-slot
-    # segments and their groups (bf16), or pairs + entry states of the token
-    # segments (fp32)
+    # enough for either path: chunk images + pairs of the chunk-slot segments +
+    # pairs and entry states of their groups (bf16), or pairs + entry states of
+    # the token segments (fp32)
     need = lib.kda_segment_scan_workspace_size(1, 128, 4, 4, 128, 128)
     slots = 128 // 64 + 1                                    # 3 chunk slots -> 3 segments
-    # images + pairs + entry states, and the same for the 2 groups of 2 segments the
-    # pairs are scanned in
-    need_bf16 = slots * 4 * 63488 + 3 * 4 * 128 * 384 * 4 + 2 * 4 * 128 * 384 * 4
+    # images + segment pairs, and pairs + entry states of the 2 groups of 2 segments
+    # the pairs are scanned in
+    need_bf16 = slots * 4 * 63488 + 3 * 4 * 128 * 256 * 4 + 2 * 4 * 128 * 384 * 4
     need_f32 = 4 * 4 * 128 * 384 * 4                         # 4 token segments
     assert need == max(need_bf16, need_f32)
     assert lib.kda_segment_scan_workspace_size(0, 128, 4, 4, 128, 128) == 0

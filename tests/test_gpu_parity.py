@@ -131,6 +131,43 @@ def test_chunk_fwd_resume_equals_one_call():
     assert np.array_equal(Sb, S_all)
 
 
+def _units_fill_device(units):
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"    (document|segment, head) units {units}, compute units {cus}: "
+          f"{'two' if units >= cus else 'one'} column tile(s) per compute wave", flush=True)
+
+
+def test_many_documents_wide_recurrence():
+    """Enough (document, head) units to fill the device: the recurrence runs
+    128 columns per workgroup.  Against the oracle and the fused kernel."""
+    rng = np.random.default_rng(35)
+    lengths = [int(x) for x in rng.integers(0, 150, size=40)] + [0, 1, 64, 65]
+    inp = kda_gen.make_prefill(35, int(sum(lengths)), 8, "bf16", lengths=lengths, s0_std=0.02,
+                               s0_docs="all")
+    _case(inp, 0)
+    _units_fill_device(inp.N * inp.H)
+    o, S = gpu_chunk_fwd(inp)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+    o2, S2 = gpu_chunk_fwd(inp, fused=True)
+    eo, _ = rel_l2_slices(o, o2, inp.cu_seqlens)
+    es, _ = rel_l2_slices(S, S2, axis_tokens=False)
+    print(f"    vs fused kernel: O {eo:.3e} S {es:.3e}", flush=True)
+    assert eo <= 1e-3 and es <= 1e-3, (eo, es)
+
+
+def test_segment_scan_many_segments_wide_recurrence():
+    """Segment pairs and re-runs with 128 columns per workgroup (enough
+    (segment, head) units to fill the device), segments of one chunk slot."""
+    inp = kda_gen.make_prefill(45, 4100, 8, "bf16", lengths=[1000, 64, 0, 2500, 536],
+                               s0_std=0.05, s0_docs="all")
+    _case(inp, 0)
+    print("    n_segments=256", flush=True)
+    _units_fill_device(69 * inp.H)  # 4100 // 64 + 5 chunk slots, one per segment
+    o, S = gpu_segment_scan(inp, n_segments=256)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+
+
 SCAN_CASES = {
     # lengths chosen so that segment boundaries fall inside documents, exactly on
     # a document start (n_seg=7 -> segments of 215 tokens; a document starts at 430),
