@@ -276,12 +276,13 @@ __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO:
 }
 
 // a2: decay factors of this thread's 4 tokens x 8 channels.  The subtile
-// operands Qh, Kh, Ki go to LDS tiles (natural channel order); per token row
-// i the sink receives K_decay and Q_decay (row_sink(i, kdec[8], qdec[8]));
-// K_restore is returned for the caller to store.
-template <class Ar, class IO, class RowSink>
+// operands Qh and Ki go to LDS tiles (natural channel order) and Kh to
+// kh_sink(r, i, kh[8]) (token 16w + 4tq + r = i); per token row i the sink
+// receives K_decay and Q_decay (row_sink(i, kdec[8], qdec[8])); K_restore is
+// returned for the caller to store.
+template <class Ar, class IO, class KhSink, class RowSink>
 __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename Ar::E *Qh,
-                                                    typename Ar::E *Kh, typename Ar::E *Ki,
+                                                    KhSink &&kh_sink, typename Ar::E *Ki,
                                                     const typename IO::raw8 (&Rq)[4],
                                                     const typename IO::raw8 (&Rk)[4],
                                                     const float (&G)[4][8], int w, int tq, int cg,
@@ -313,8 +314,7 @@ __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename 
     }
     Ar::store4(&Qh[TD::idx(i, 8 * cg)], qh);
     Ar::store4(&Qh[TD::idx(i, 8 * cg + 4)], qh + 4);
-    Ar::store4(&Kh[TD::idx(i, 8 * cg)], kh);
-    Ar::store4(&Kh[TD::idx(i, 8 * cg + 4)], kh + 4);
+    kh_sink(r, i, kh);
     Ar::store4(&Ki[TD::idx(i, 8 * cg)], ki);
     Ar::store4(&Ki[TD::idx(i, 8 * cg + 4)], ki + 4);
     row_sink(i, kdec, qdec);
@@ -335,14 +335,17 @@ __device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
 // a3: A_qk and A_kk per subtile pair (I >= J); wave w takes pairs w, w+4, w+8.
 // Products are formed transposed, (K_inv_J)(Q_I)^T, so lane (g, j) ends up
 // with row j of the pair's tile at columns 4g..4g+3 and writes them at once.
-// L (fp32, natural order) goes to LDS; M_qk goes to mqk_sink(row, J, mq[4]).
-template <class Ar, class MqkSink>
+// L (natural order, operand precision) goes to LDS; M_qk goes to
+// mqk_sink(row, J, mq[4]).  PRODUCTS selects M_qk (1), L (2) or both (3); a
+// product not selected reads nothing from its tile (Qh or Kh).
+constexpr int PROD_MQK = 1, PROD_L = 2;
+template <class Ar, int PRODUCTS, class MqkSink>
 __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const typename Ar::E *Qh,
                                                       const typename Ar::E *Kh,
-                                                      const typename Ar::E *Ki, float *L, int w,
-                                                      int g, int j, MqkSink &&mqk_sink) {
+                                                      const typename Ar::E *Ki, typename Ar::E *L,
+                                                      int w, int g, int j, MqkSink &&mqk_sink) {
   using BReg = typename Ar::BReg;
-  using TL = Tile<float, CH>;
+  using TL = Tile<typename Ar::E, CH>;
   for (int pidx = w; pidx < 10; pidx += 4) {
     const int I = (pidx == 0) ? 0 : (pidx < 3 ? 1 : (pidx < 6 ? 2 : 3));
     const int J = pidx - I * (I + 1) / 2;
@@ -356,8 +359,8 @@ __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const t
         const int fp = I * (I - 1) / 2 + J;
         kin = Ar::template breg_lds_scaled<D>(Ki, 16 * J + j, kb, g, ps.F[fp]);
       }
-      aq = Ar::template k32_regA<D>(aq, kin, Qh, 16 * I + j, kb, g);
-      ak = Ar::template k32_regA<D>(ak, kin, Kh, 16 * I + j, kb, g);
+      if constexpr ((PRODUCTS & PROD_MQK) != 0) aq = Ar::template k32_regA<D>(aq, kin, Qh, 16 * I + j, kb, g);
+      if constexpr ((PRODUCTS & PROD_L) != 0) ak = Ar::template k32_regA<D>(ak, kin, Kh, 16 * I + j, kb, g);
     }
     // lane (g, j): element r is (row j of subtile I, column 4g + r of subtile J)
     const int row = 16 * I + j;
@@ -369,8 +372,8 @@ __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const t
       mq[r] = (I > J || col <= j) ? aq[r] : 0.f;        // diagonal kept
       lk[r] = (I > J || col < j) ? bi * ak[r] : 0.f;    // strictly lower
     }
-    mqk_sink(row, J, mq);
-    *reinterpret_cast<float4 *>(&L[TL::idx(row, 16 * J + 4 * g)]) = make_float4(lk[0], lk[1], lk[2], lk[3]);
+    if constexpr ((PRODUCTS & PROD_MQK) != 0) mqk_sink(row, J, mq);
+    if constexpr ((PRODUCTS & PROD_L) != 0) Ar::store4(&L[TL::idx(row, 16 * J + 4 * g)], lk);
   }
 }
 
@@ -406,15 +409,14 @@ __device__ __forceinline__ floatx4 unit_lower_inverse(floatx4 Ln, floatx4 Lt, in
 // a4 (i): inverse of the diagonal block w of I + L, stored to Tdg[w] (row-major)
 // and returned in accumulator layout.
 template <class Ar>
-__device__ __forceinline__ floatx4 prep_diag_inverse(const float *L, typename Ar::E (*Tdg)[SUB * SUB],
-                                                     int w, int g, int j) {
-  using TL = Tile<float, CH>;
+__device__ __forceinline__ floatx4 prep_diag_inverse(const typename Ar::E *L,
+                                                     typename Ar::E (*Tdg)[SUB * SUB], int w, int g,
+                                                     int j) {
+  using TL = Tile<typename Ar::E, CH>;
   floatx4 Ln, Lt;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    Ln[r] = L[TL::idx(16 * w + 4 * g + r, 16 * w + j)];  // L (rows 4g+r, col j)
-    Lt[r] = L[TL::idx(16 * w + j, 16 * w + 4 * g + r)];  // L^T
-  }
+  for (int r = 0; r < 4; ++r) Ln[r] = Ar::tof(L[TL::idx(16 * w + 4 * g + r, 16 * w + j)]);  // L (rows 4g+r, col j)
+  Lt = Ar::load4(&L[TL::idx(16 * w + j, 16 * w + 4 * g)]);                               // L^T
   const floatx4 T = unit_lower_inverse<Ar>(Ln, Lt, g, j);
 #pragma unroll
   for (int r = 0; r < 4; ++r) Tdg[w][(4 * g + r) * SUB + j] = Ar::cvt(T[r]);
@@ -426,11 +428,12 @@ __device__ __forceinline__ floatx4 prep_diag_inverse(const float *L, typename Ar
 // all tiles in registers (accumulator layout doubles as the 16x16x16 B operand).
 // Stores INV Diag(beta) into the 64x64 tile INVb with the token axis permuted.
 template <class Ar, int J>
-__device__ __forceinline__ void inv_block_column(const float *L, const typename Ar::E (*Tdg)[SUB * SUB],
+__device__ __forceinline__ void inv_block_column(const typename Ar::E *L,
+                                                 const typename Ar::E (*Tdg)[SUB * SUB],
                                                  const float *beta, typename Ar::E *INVb,
                                                  floatx4 Tjj, int g, int j) {
   using TC = Tile<typename Ar::E, CH>;
-  using TL = Tile<float, CH>;
+  using TL = TC;
   floatx4 X[4];
   X[J] = Tjj;
 #pragma unroll
@@ -438,8 +441,7 @@ __device__ __forceinline__ void inv_block_column(const float *L, const typename 
     floatx4 R = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int K = J; K < I; ++K) {
-      const float4 l4 = *reinterpret_cast<const float4 *>(&L[TL::idx(16 * I + j, 16 * K + 4 * g)]);
-      R = Ar::k16(R, floatx4{l4.x, l4.y, l4.z, l4.w}, X[K]);
+      R = Ar::k16(R, Ar::load4(&L[TL::idx(16 * I + j, 16 * K + 4 * g)]), X[K]);
     }
     const floatx4 t = Ar::load4(&Tdg[I][j * SUB + 4 * g]);  // row j of T_II
     floatx4 Y = {0.f, 0.f, 0.f, 0.f};
@@ -457,7 +459,7 @@ __device__ __forceinline__ void inv_block_column(const float *L, const typename 
 
 // a4 (ii): wave w completes block column w (runtime wave index -> template).
 template <class Ar>
-__device__ __forceinline__ void prep_block_columns(const float *L,
+__device__ __forceinline__ void prep_block_columns(const typename Ar::E *L,
                                                    const typename Ar::E (*Tdg)[SUB * SUB],
                                                    const float *beta, typename Ar::E *INVb,
                                                    floatx4 Tww, int w, int g, int j) {

@@ -41,7 +41,7 @@ struct __align__(16) FwdSmem {
   POps<E, ALIAS> A;
   E Mqk[CH * CH];    // token (column) axis permuted; upper 16x16 blocks stay 0
   E INVb[CH * CH];   // INV Diag(beta); token axis permuted; upper blocks stay 0
-  float L[CH * CH];  // strict lower part used
+  E L[CH * CH];      // strict lower part used
   E Tdg[4][SUB * SUB];  // inverses of the diagonal 16x16 blocks of I + L
   float gamC[D];        // gamma^C = e^(G_C)
   PrepLds ps;
@@ -234,7 +234,13 @@ __global__ void __launch_bounds__(FWD_THREADS, 1) kda_fwd_kernel(FwdParams p) {
 
     float Kres[4][8];
     float Kdec_s[4][8], Qdec_s[4][8];  // fp32 build: held until phase 1 is consumed
-    prep_decay_operands<Ar, IO>(sm.ps, sm.A.p1.Qh, sm.A.p1.Kh, sm.A.p1.Ki, Rq, Rk, G, w, tq, cg, Kres,
+    prep_decay_operands<Ar, IO>(sm.ps, sm.A.p1.Qh,
+                                [&](int, int i, const float *kh) {
+                                  using TD = Tile<typename Ar::E, D>;
+                                  Ar::store4(&sm.A.p1.Kh[TD::idx(i, 8 * cg)], kh);
+                                  Ar::store4(&sm.A.p1.Kh[TD::idx(i, 8 * cg + 4)], kh + 4);
+                                },
+                                sm.A.p1.Ki, Rq, Rk, G, w, tq, cg, Kres,
                                 [&](int i, const float *kdec, const float *qdec) {
                                   if constexpr (!ALIAS) {
                                     write_phase2_row<Ar>(sm, kdec, qdec, i, cg);
@@ -256,7 +262,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 1) kda_fwd_kernel(FwdParams p) {
     __syncthreads();  // B3
     SCHED_FENCE();
 
-    prep_subtile_products<Ar>(sm.ps, sm.A.p1.Qh, sm.A.p1.Kh, sm.A.p1.Ki, sm.L, w, g, j,
+    prep_subtile_products<Ar, PROD_MQK | PROD_L>(sm.ps, sm.A.p1.Qh, sm.A.p1.Kh, sm.A.p1.Ki, sm.L, w, g, j,
                               [&](int row, int J, const float *mq) {
                                 Ar::store4(&sm.Mqk[TC::idx(row, kperm(16 * J + 4 * g))], mq);
                               });

@@ -69,21 +69,24 @@ __device__ __forceinline__ void img_st4(__amdgpu_buffer_rsrc_t r, int off, const
 // ---------------------------------------------------------------------------
 // Prep: one workgroup per (chunk slot, head).
 // ---------------------------------------------------------------------------
+// 51 KB, so that three workgroups share a compute unit: the query- and
+// key-side subtile operands take turns in one tile (M_qk is formed first, then
+// the key side, held in registers meanwhile, overwrites the query side for L).
 struct __align__(16) PrepSmem {
   union {
     struct {
-      bf16_t Qh[CH * D];  // q_i e^(G_i - G_s(i))
-      bf16_t Kh[CH * D];  // k_i e^(G_i - G_s(i))
-      bf16_t Ki[CH * D];  // k_j e^(G_s(j) - G_j)
+      bf16_t QKh[CH * D];  // q_i e^(G_i - G_s(i)), then k_i e^(G_i - G_s(i))
+      bf16_t Ki[CH * D];   // k_j e^(G_s(j) - G_j)
     } p1;
     bf16_t INVb[CH * CH];  // staged after the subtile operands are dead
   } u;
-  float L[CH * CH];
+  bf16_t L[CH * CH];
   bf16_t Tdg[4][SUB * SUB];
   PrepLds ps;
 };
+static_assert(3 * sizeof(PrepSmem) <= 160 * 1024, "three prep workgroups per compute unit");
 
-__global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitParams p) {
+__global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitParams p) {
   using Ar = Arith<false>;
   using IO = bufio<bf16_t>;
   using TD = Tile<bf16_t, D>;
@@ -144,7 +147,13 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitPar
   const __amdgpu_buffer_rsrc_t ri =
       make_rsrc((char *)p.ws + ((int64_t)h * p.n_slots + slot) * IMG_BYTES, IMG_BYTES);
   float Kres[4][8];
-  prep_decay_operands<Ar, IO>(sm.ps, sm.u.p1.Qh, sm.u.p1.Kh, sm.u.p1.Ki, Rq, Rk, G, w, tq, cg, Kres,
+  bf16x4 kh_keep[4][2];  // key-side subtile operand of this thread's 4 tokens x 8 channels
+  prep_decay_operands<Ar, IO>(sm.ps, sm.u.p1.QKh,
+                              [&](int r, int, const float *kh) {
+                                kh_keep[r][0] = to_bf16x4(floatx4{kh[0], kh[1], kh[2], kh[3]});
+                                kh_keep[r][1] = to_bf16x4(floatx4{kh[4], kh[5], kh[6], kh[7]});
+                              },
+                              sm.u.p1.Ki, Rq, Rk, G, w, tq, cg, Kres,
                               [&](int i, const float *kdec, const float *qdec) {
                                 const int c0 = 2 * TD::idx(i, kperm(8 * cg));
                                 const int c1b = 2 * TD::idx(i, kperm(8 * cg + 4));
@@ -163,10 +172,22 @@ __global__ void __launch_bounds__(FWD_THREADS, 2) kda_chunk_prep_kernel(SplitPar
   __syncthreads();
   SCHED_FENCE();
 
-  prep_subtile_products<Ar>(sm.ps, sm.u.p1.Qh, sm.u.p1.Kh, sm.u.p1.Ki, sm.L, w, g, j,
-                            [&](int row, int J, const float *mq) {
-                              img_st4(ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(16 * J + 4 * g)), mq);
-                            });
+  prep_subtile_products<Ar, PROD_MQK>(sm.ps, sm.u.p1.QKh, nullptr, sm.u.p1.Ki, sm.L, w, g, j,
+                                      [&](int row, int J, const float *mq) {
+                                        img_st4(ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(16 * J + 4 * g)), mq);
+                                      });
+  __syncthreads();  // the query side is consumed
+  SCHED_FENCE();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * w + 4 * tq + r;
+    *reinterpret_cast<bf16x4 *>(&sm.u.p1.QKh[TD::idx(i, 8 * cg)]) = kh_keep[r][0];
+    *reinterpret_cast<bf16x4 *>(&sm.u.p1.QKh[TD::idx(i, 8 * cg + 4)]) = kh_keep[r][1];
+  }
+  __syncthreads();
+  SCHED_FENCE();
+  prep_subtile_products<Ar, PROD_L>(sm.ps, nullptr, sm.u.p1.QKh, sm.u.p1.Ki, sm.L, w, g, j,
+                                    [](int, int, const float *) {});
   // The recurrence reads the upper blocks (0,1) and (2,3) of M_qk and INV Diag(beta)
   // (its 32-wide k steps span two subtiles); they must hold zeros.
   const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -393,18 +414,25 @@ __device__ __forceinline__ int64_t next_chunk_slot(const SplitParams &p, int64_t
   return s;
 }
 
-// Parts of the image the L2 touches cover, in 64-byte lines: all operands, or
-// for segment pairs only K_decay, K_restore^T, INV Diag(beta) and gamma^C.
-constexpr int IMG_LINES_ALL = (OFF_GAMC + 4 * D) / 64;
-constexpr int KD_LINES = (OFF_QD - OFF_KD) / 64;
-constexpr int KRT_LINES = (OFF_MQK - OFF_KRT) / 64;
-constexpr int IMG_LINES_PAIRS = KD_LINES + KRT_LINES + (OFF_GAMC + 4 * D - OFF_INVB) / 64;
+// L2 prefetch touches: one dword per L2 line (128 bytes) pulls the line in.
+// Each touch holds one of the compute unit's outstanding L1 miss slots for a
+// whole memory latency, the slots the copies need as well, so there is one per
+// line and no more.  Parts of the image they cover: all operands, or for
+// segment pairs only K_decay, K_restore^T, INV Diag(beta) and gamma^C.
+constexpr int TOUCH_LINE = 128;
+constexpr int IMG_LINES_ALL = (OFF_GAMC + 4 * D + TOUCH_LINE - 1) / TOUCH_LINE;
+constexpr int KD_LINES = (OFF_QD - OFF_KD) / TOUCH_LINE;
+constexpr int KRT_LINES = (OFF_MQK - OFF_KRT) / TOUCH_LINE;
+constexpr int IMG_LINES_PAIRS = KD_LINES + KRT_LINES + (OFF_GAMC + 4 * D - OFF_INVB) / TOUCH_LINE;
 static_assert(OFF_KD == 0 && OFF_GAMC == OFF_INVB + 2 * PackedLower::ELEMS, "image layout");
+static_assert((OFF_QD - OFF_KD) % TOUCH_LINE == 0 && (OFF_MQK - OFF_KRT) % TOUCH_LINE == 0 &&
+                  (OFF_GAMC + 4 * D - OFF_INVB) % TOUCH_LINE == 0 && OFF_INVB % TOUCH_LINE == 0,
+              "touched parts must be whole lines");
 __device__ __forceinline__ int touch_line_offset(int line, bool pairs_only) {
-  if (!pairs_only) return 64 * line;
-  if (line < KD_LINES) return 64 * line;
-  if (line < KD_LINES + KRT_LINES) return OFF_KRT + 64 * (line - KD_LINES);
-  return OFF_INVB + 64 * (line - KD_LINES - KRT_LINES);
+  if (!pairs_only) return TOUCH_LINE * line;
+  if (line < KD_LINES) return TOUCH_LINE * line;
+  if (line < KD_LINES + KRT_LINES) return OFF_KRT + TOUCH_LINE * (line - KD_LINES);
+  return OFF_INVB + TOUCH_LINE * (line - KD_LINES - KRT_LINES);
 }
 
 // Items: documents (rmode 0), or segments of seg_slots chunk slots (rmode 1:
@@ -498,13 +526,14 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
     // dword per 64 bytes.  Always exactly TOUCH_OPS operations per wave
     // (offsets past the data, or a slot past the range, fetch nothing), so the
     // wait at the top of the loop can leave exactly these in flight.
-    constexpr int TOUCH_IMG = NT == 1 ? 2 : 4;
+    // (worst case: NT = 2 outside pair mode, one workgroup touches the whole image)
+    constexpr int TOUCH_IMG = (NT == 1 ? (IMG_LINES_ALL + 1) / 2 : IMG_LINES_ALL) / REC_COPY_THREADS + 1;
     constexpr int TOUCH_OPS = TOUCH_IMG + 1;
     constexpr int OOB = 1 << 30;
-    constexpr int VLINES = SLICE * ES / 64;  // 64-byte lines per v row
+    constexpr int VLINES = (SLICE * ES + TOUCH_LINE - 1) / TOUCH_LINE;  // lines per v row
     static_assert(CH * VLINES <= REC_COPY_THREADS, "v touch coverage");
-    static_assert((IMG_LINES_ALL + 1) / 2 <= TOUCH_IMG * REC_COPY_THREADS || NT == 2, "touch coverage");
-    static_assert(IMG_LINES_ALL <= 4 * REC_COPY_THREADS, "touch coverage");
+    static_assert(TOUCH_IMG * REC_COPY_THREADS >= (NT == 1 ? (IMG_LINES_ALL + 1) / 2 : IMG_LINES_ALL),
+                  "touch coverage");
     const int n_lines = pairs_only ? IMG_LINES_PAIRS : IMG_LINES_ALL;
     const int part_lines = (n_lines + nsplit - 1) / nsplit;
     auto issue_touch = [&](int64_t sl) {
@@ -518,7 +547,7 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
         touch4_to_lds(ri, lds_sink, k < part_lines && line < n_lines ? touch_line_offset(line, pairs_only) : OOB);
       }
       touch4_to_lds(v_rsrc(c, in_range), lds_sink,
-                    ct < CH * VLINES ? (ct / VLINES) * rowb + (ct % VLINES) * 64 : OOB);
+                    ct < CH * VLINES ? (ct / VLINES) * rowb + (ct % VLINES) * TOUCH_LINE : OOB);
     };
     constexpr int AHEAD = 2;  // slots between a touch and the copy that uses it
 
