@@ -80,6 +80,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="prefill",
+                    help="prefill: the single-sequence H=96 step (the reported metric); long: "
+                         "the T=262144 H=8 segment scan; varlen: the packed 65536-token H=96 "
+                         "batch (context lines with their own config)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (used to "
                          "scale the HBM byte counters of a profiler) and exit")
@@ -126,6 +130,64 @@ def _events(torch, stream, n):
             for _ in range(n)]
 
 
+def other_workload(args, np, torch, kda_gen, kda, dev):
+    """One JSON line for the long-prefill segment scan or the packed varlen batch:
+    tokens/s over the timed steps and the fraction of the FlashKDA model bound
+    (bytes and FLOPs per chunk-head, over the chunks the documents actually have)."""
+    idx = 2 if args.workload == "long" else 3
+    inp = kda_gen.workload(idx)
+    T, H, N = inp.T, inp.H, inp.N
+    t = {n: kda_gen.to_torch(getattr(inp, n), dev) for n in ("q", "k", "v", "z", "beta")}
+    A_log = torch.from_numpy(inp.A_log).to(dev)
+    S0 = torch.from_numpy(inp.S0).to(dev) if inp.S0 is not None else None
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if N > 1 else None
+    cu_host = inp.cu_seqlens if N > 1 else None
+    o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+    if args.workload == "long":
+        n_seg = kda.kda_default_segments()
+        ws = torch.empty(kda.kda_segment_scan_workspace_size(N, T, H, n_seg), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            kda.kda_segment_scan(t["q"], t["k"], t["v"], t["z"], t["beta"], A_log, inp.g_min, S0,
+                                 cu, cu_host, n_segments=n_seg, o=o, final_state=fin, workspace=ws)
+        config = {"workload": f"long prefill, one sequence B=1 H={H} T={T} d=128 bf16, "
+                              f"segment scan with {n_seg} segments (one per compute unit)",
+                  "global_batch": 1, "seq_len": T, "heads": H, "parallelism": "single GPU"}
+    else:
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_size(N, T, H), dtype=torch.uint8, device=dev)
+
+        def step():
+            kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], A_log, inp.g_min, S0, cu,
+                              cu_host, o=o, final_state=fin, workspace=ws)
+        config = {"workload": f"packed varlen prefill, {T} tokens in {N} documents (log-uniform "
+                              f"lengths in [64, 16384]), H={H} d=128 bf16, state reset per document",
+                  "global_batch": N, "seq_len": T, "heads": H, "parallelism": "single GPU"}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    lens = np.diff(inp.cu_seqlens.astype(np.int64)) if N > 1 else np.array([T])
+    chunk_heads = int(np.sum((lens + 63) // 64)) * H
+    model_bytes = chunk_heads * bytes_model_per_chunk() + N * H * state_bytes()
+    model_flops = chunk_heads * flops_model_per_chunk()
+    t_model = max(model_bytes / (HBM_PEAK_GBPS * 1e9), model_flops / (BF16_PEAK_TFLOPS * 1e12))
+    print(json.dumps({
+        "metric": f"KDA {args.workload} prefill tokens/s", "value": T / (ms * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": config,
+        "model_roofline": {"model": "FlashKDA bytes 8C^2+22CD and FLOPs 12C^3+8C^2D+6CD^2 per chunk-head",
+                           "chunk_heads": chunk_heads, "bytes": model_bytes, "flops": model_flops,
+                           "t_bound_ms": t_model * 1e3, "frac": t_model / (ms * 1e-3)}}))
+    return 0
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -145,6 +207,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.workload != "prefill":
+        return other_workload(args, np, torch, kda_gen, kda, dev)
 
     # ---------------- prefill: single sequence, H=96, T=8192, bf16 ----------
     inp = kda_gen.workload(1)
