@@ -139,11 +139,26 @@ int64_t scan_groups(int64_t n_seg) {
   const int64_t g = scan_group_len(n_seg);
   return (n_seg + g - 1) / g;
 }
+// Chunk slots up to and including the last one that holds a chunk: the
+// segments of the two-kernel path divide these (the slot after a document whose
+// length is a multiple of 64, and the slots of trailing empty documents, hold
+// none; leaving them out keeps the segments, and so the passes over them, as
+// short as the requested count allows).
+int64_t used_chunk_slots(int64_t T, int32_t N, const int32_t *cu_host) {
+  for (int32_t d = N - 1; d >= 0; --d) {
+    const int64_t a = cu_host ? cu_host[d] : 0, b = cu_host ? cu_host[d + 1] : T;
+    if (b > a) return kda::first_slot(a, d) + (b - a + 63) / 64;
+  }
+  return 0;
+}
 size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
-  const SegPlan sp = plan_segments(kda::n_chunk_slots(T, N), requested);
+  // sized for the most segments any plan over at most n_chunk_slots units can
+  // give (min(requested, units)), and for their groups (at most the group length)
+  int64_t n_max = requested < 1 ? 1 : requested;
+  if (n_max > kda::n_chunk_slots(T, N)) n_max = kda::n_chunk_slots(T, N);
   // chunk images, segment pairs [., D, 2D], group pairs and group entry states
-  return kda::split_workspace_bytes(T, N, H) + (size_t)sp.n_seg * H * kD * 2 * kD * sizeof(float) +
-         scan_workspace(scan_groups(sp.n_seg), H);
+  return kda::split_workspace_bytes(T, N, H) + (size_t)n_max * H * kD * 2 * kD * sizeof(float) +
+         scan_workspace(scan_group_len(n_max), H);
 }
 
 }  // namespace
@@ -304,7 +319,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     // on the recurrence kernel; segments are ranges of chunk slots
     const int64_t n_slots = kda::n_chunk_slots(T, N);
     if (n_slots * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
-    const SegPlan sp = plan_segments(n_slots, req);
+    const SegPlan sp = plan_segments(used_chunk_slots(T, N, cu_seqlens_host), req);
     if (sp.n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
     const size_t need = split_scan_workspace(T, N, H, req);
     if (!workspace || workspace_bytes < need)
