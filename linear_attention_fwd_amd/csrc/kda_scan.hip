@@ -174,30 +174,32 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
 //     pair, X_i, is written to states[i]; X <- M_i X + S~_i;
 //   mode 1 (compose): X = [S~ | M] of the first pair, then X <- M_i X + [S~_i | 0]
 //     for the others, i.e. the pairs composed into one; written to composed[chain].
-// One workgroup per (chain, head, slice of 16 CHAIN_TILES columns of X); each
-// of the 4 waves owns 32 rows and every 16-column tile of the slice, so every
-// M row it loads (and splits into bf16 halves) serves all of them.  Same step as the pair
-// scan: M rows as the A operand from the pair array (the next step's loaded
-// during the current one), the X slice from LDS (double-buffered), products in
-// bf16 hi/lo halves (three MFMAs per k block and tile).
+// One workgroup per (chain, head, slice of 16 CT columns of X) with 8 / RT
+// waves; wave w owns rows 16 RT w .. 16 RT (w + 1) - 1 and every 16-column
+// tile of the slice, so every M row it loads (and splits into bf16 halves)
+// serves CT tiles.  Same step as the pair scan: M rows as the A operand from
+// the pair array (the next step's loaded during the current one), the X slice
+// from LDS (double-buffered), products in bf16 hi/lo halves (three MFMAs per k
+// block and tile).
 // ---------------------------------------------------------------------------
-template <int CHAIN_TILES> struct ChainOps {
-  float4 m[2][4][2];              // [row tile][kb][half]: M rows 32w + 16t + j
-  floatx4 st[CHAIN_TILES][2];     // [column tile][row tile]: S~ (not used on M columns)
+template <int CT, int RT> struct ChainOps {
+  float4 m[RT][4][2];  // [row tile][kb][half]: M rows 16 RT w + 16 t + j
+  floatx4 st[CT][RT];  // [column tile][row tile]: S~ (0 on M columns, read out of bounds)
 };
 
-template <int CHAIN_TILES>
-__global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanChains sc) {
-  constexpr int CHAIN_COLS = 16 * CHAIN_TILES;
-  using Ops = ChainOps<CHAIN_TILES>;
-  __shared__ __align__(16) float XT[2][CHAIN_COLS][D];  // X slice, [buffer][column][row]
+template <int CT, int RT>
+__global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc) {
+  constexpr int COLS = 16 * CT;
+  constexpr int ROWS = 16 * RT;  // rows per wave
+  using Ops = ChainOps<CT, RT>;
+  __shared__ __align__(16) float XT[2][COLS][D];  // X slice, [buffer][column][row]
 
-  const int nslices = sc.ncols / CHAIN_COLS;
+  const int nslices = sc.ncols / COLS;
   const ScanBlock sb = scan_block(nslices);
   if (sb.unit >= sc.n_chains * sc.H) return;
   const int chain = sb.unit / sc.H;
   const int h = sb.unit % sc.H;
-  const int c0 = CHAIN_COLS * sb.slice;  // first column of the slice (S~ part below D, M part from D on)
+  const int c0 = COLS * sb.slice;  // first column of the slice (S~ part below D, M part from D on)
   const int first = chain * sc.chain_len;
   const int last = min(first + sc.chain_len, sc.n_pairs);
   if (first >= last) return;
@@ -208,44 +210,48 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
   const int j = lane & 15;
   const bool st_on = c0 < D;  // the slice lies in the S~ columns (D is a multiple of the slice)
 
-  auto row_of = [&](int t, int r) { return 32 * w + 16 * t + 4 * g + r; };
+  auto row_of = [&](int t, int r) { return ROWS * w + 16 * t + 4 * g + r; };
   auto col_of = [&](int c) { return c0 + 16 * c + j; };
   auto pair_at = [&](int i) { return sc.pairs + ((int64_t)i * sc.H + h) * (D * 2 * D); };
-  auto share = [&](int buf, const floatx4 (&X)[CHAIN_TILES][2]) {
+  auto share = [&](int buf, const floatx4 (&X)[CT][RT]) {
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) XT[buf][16 * c + j][row_of(t, r)] = X[c][t][r];
   };
   // Global accesses go through buffer descriptors: one per-lane offset, with
   // the per-element constants in the scalar offset, so that no array of
   // per-element addresses has to stay live across the loop.
-  auto write_state = [&](float *dst, int ld, const floatx4 (&X)[CHAIN_TILES][2]) {
+  auto write_state = [&](float *dst, int ld, const floatx4 (&X)[CT][RT]) {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst, D * ld * 4);
-    const int voff = ((32 * w + 4 * g) * ld + c0 + j) * 4;
+    const int voff = ((ROWS * w + 4 * g) * ld + c0 + j) * 4;
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(X[c][t][r]), rd, voff,
                                                 ((16 * t + r) * ld + 16 * c) * 4, 0);
   };
   auto load_ops = [&](int i, Ops &o) {
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(pair_at(i), D * 2 * D * 4);
-    const int voff_st = ((32 * w + 4 * g) * (2 * D) + (c0 & (D - 1)) + j) * 4;
-    const int voff_m = ((32 * w + j) * (2 * D) + D + 8 * g) * 4;
+    const float *P = pair_at(i);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(P, D * 2 * D * 4);
+    // S~ through a descriptor of size 0 on the M columns: those loads return 0
+    // and move no data
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(P, st_on ? D * 2 * D * 4 : 0);
+    const int voff_st = ((ROWS * w + 4 * g) * (2 * D) + (c0 & (D - 1)) + j) * 4;
+    const int voff_m = ((ROWS * w + j) * (2 * D) + D + 8 * g) * 4;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < RT; ++t) {
 #pragma unroll
-      for (int c = 0; c < CHAIN_TILES; ++c)
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)  // S~ (a load either way; zeroed for the M columns where used)
+        for (int r = 0; r < 4; ++r)
           o.st[c][t][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rp, voff_st, ((16 * t + r) * (2 * D) + 16 * c) * 4, 0));
+              rs, voff_st, ((16 * t + r) * (2 * D) + 16 * c) * 4, 0));
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -257,18 +263,17 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
         }
     }
   };
-  auto apply = [&](int pb, const Ops &o, floatx4 (&X)[CHAIN_TILES][2]) {
-    floatx4 acc[CHAIN_TILES][2];
-    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto apply = [&](int pb, const Ops &o, floatx4 (&X)[CT][RT]) {
+    floatx4 acc[CT][RT];
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) acc[c][t] = st_on ? o.st[c][t] : zero;
+      for (int t = 0; t < RT; ++t) acc[c][t] = o.st[c][t];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 ah[2], al[2];  // rows of M, both row tiles
+      bf16x8 ah[RT], al[RT];  // rows of M
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < RT; ++t) {
         const float4 a0 = o.m[t][kb][0], a1 = o.m[t][kb][1];
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
@@ -278,7 +283,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
         }
       }
 #pragma unroll
-      for (int c = 0; c < CHAIN_TILES; ++c) {
+      for (int c = 0; c < CT; ++c) {
         const float4 b0 = *reinterpret_cast<const float4 *>(&XT[pb][16 * c + j][32 * kb + 8 * g]);
         const float4 b1 = *reinterpret_cast<const float4 *>(&XT[pb][16 * c + j][32 * kb + 8 * g + 4]);
         const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
           bl[e] = (__bf16)(bv[e] - (float)bh[e]);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < RT; ++t) {
           acc[c][t] = mfma_bf16_k32(al[t], bh, acc[c][t]);
           acc[c][t] = mfma_bf16_k32(ah[t], bl, acc[c][t]);
           acc[c][t] = mfma_bf16_k32(ah[t], bh, acc[c][t]);
@@ -297,28 +302,28 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
       }
     }
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) X[c][t] = acc[c][t];
+      for (int t = 0; t < RT; ++t) X[c][t] = acc[c][t];
   };
 
-  floatx4 X[CHAIN_TILES][2];
+  floatx4 X[CT][RT];
   int i0;  // first pair applied
   if (sc.mode == 1) {
     const float *P = pair_at(first);
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) X[c][t][r] = P[row_of(t, r) * (2 * D) + col_of(c)];
     i0 = first + 1;
   } else {
     const float *src = sc.init ? sc.init + ((int64_t)chain * sc.H + h) * (D * D) : nullptr;
 #pragma unroll
-    for (int c = 0; c < CHAIN_TILES; ++c)
+    for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) X[c][t][r] = src ? src[row_of(t, r) * D + col_of(c)] : 0.f;
     i0 = first;
@@ -350,17 +355,21 @@ __global__ void __launch_bounds__(SCAN_THREADS, 2) kda_scan_chains_kernel(ScanCh
   if (sc.mode == 1) write_state(sc.composed + ((int64_t)chain * sc.H + h) * (D * 2 * D), 2 * D, X);
 }
 
-// Two tiles per wave when the chains alone give enough workgroups to fill the
-// device twice over (each step then costs more but serves twice the columns);
-// one otherwise, where the step latency of few workgroups decides.
+// The widest slice that still gives every compute unit a workgroup: each step
+// then streams M once for more columns.  Chains too few for that (the scan of
+// the group pairs) take 16 columns per workgroup, where the step latency of
+// few workgroups decides.
 hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream) {
   const int64_t units = (int64_t)sc.n_chains * sc.H;
-  if (units * (sc.ncols / 32) >= 2 * (int64_t)n_cu) {
-    hipLaunchKernelGGL(kda_scan_chains_kernel<2>, dim3(scan_grid(units, sc.ncols / 32)),
-                       dim3(SCAN_THREADS), 0, stream, sc);
+  if (units * (sc.ncols / 64) >= (int64_t)n_cu) {
+    hipLaunchKernelGGL((kda_scan_chains_kernel<4, 1>), dim3(scan_grid(units, sc.ncols / 64)), dim3(512),
+                       0, stream, sc);
+  } else if (units * (sc.ncols / 32) >= 2 * (int64_t)n_cu) {
+    hipLaunchKernelGGL((kda_scan_chains_kernel<2, 2>), dim3(scan_grid(units, sc.ncols / 32)), dim3(256),
+                       0, stream, sc);
   } else {
-    hipLaunchKernelGGL(kda_scan_chains_kernel<1>, dim3(scan_grid(units, sc.ncols / 16)),
-                       dim3(SCAN_THREADS), 0, stream, sc);
+    hipLaunchKernelGGL((kda_scan_chains_kernel<1, 2>), dim3(scan_grid(units, sc.ncols / 16)), dim3(256),
+                       0, stream, sc);
   }
   return hipGetLastError();
 }
