@@ -179,8 +179,8 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
 // tile of the slice, so every M row it loads (and splits into bf16 halves)
 // serves CT tiles.  Same step as the pair scan: M rows as the A operand from
 // the pair array (the next step's loaded during the current one), the X slice
-// from LDS (double-buffered), products in bf16 hi/lo halves (three MFMAs per k
-// block and tile).
+// from LDS (double-buffered, split into bf16 halves once by its owner),
+// products in bf16 hi/lo halves (three MFMAs per k block and tile).
 // ---------------------------------------------------------------------------
 template <int CT, int RT> struct ChainOps {
   float4 m[RT][4][2];  // [row tile][kb][half]: M rows 16 RT w + 16 t + j
@@ -192,7 +192,10 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
   constexpr int COLS = 16 * CT;
   constexpr int ROWS = 16 * RT;  // rows per wave
   using Ops = ChainOps<CT, RT>;
-  __shared__ __align__(16) float XT[2][COLS][D];  // X slice, [buffer][column][row]
+  // X slice split into bf16 high and low halves by the wave that owns each
+  // value, so the B operands are read ready-made: [buffer][column][row]
+  __shared__ __align__(16) bf16_t XH[2][COLS][D];
+  __shared__ __align__(16) bf16_t XL[2][COLS][D];
 
   const int nslices = sc.ncols / COLS;
   const ScanBlock sb = scan_block(nslices);
@@ -217,9 +220,16 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+      for (int t = 0; t < RT; ++t) {
+        bf16x4 hi, lo;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) XT[buf][16 * c + j][row_of(t, r)] = X[c][t][r];
+        for (int r = 0; r < 4; ++r) {
+          hi[r] = (__bf16)X[c][t][r];
+          lo[r] = (__bf16)(X[c][t][r] - (float)hi[r]);
+        }
+        *reinterpret_cast<bf16x4 *>(&XH[buf][16 * c + j][row_of(t, 0)]) = hi;
+        *reinterpret_cast<bf16x4 *>(&XL[buf][16 * c + j][row_of(t, 0)]) = lo;
+      }
   };
   // Global accesses go through buffer descriptors: one per-lane offset, with
   // the per-element constants in the scalar offset, so that no array of
@@ -284,15 +294,8 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
       }
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const float4 b0 = *reinterpret_cast<const float4 *>(&XT[pb][16 * c + j][32 * kb + 8 * g]);
-        const float4 b1 = *reinterpret_cast<const float4 *>(&XT[pb][16 * c + j][32 * kb + 8 * g + 4]);
-        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        bf16x8 bh, bl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bh[e] = (__bf16)bv[e];
-          bl[e] = (__bf16)(bv[e] - (float)bh[e]);
-        }
+        const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&XH[pb][16 * c + j][32 * kb + 8 * g]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&XL[pb][16 * c + j][32 * kb + 8 * g]);
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           acc[c][t] = mfma_bf16_k32(al[t], bh, acc[c][t]);
@@ -356,7 +359,8 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
 }
 
 // The widest slice that still gives every compute unit a workgroup: each step
-// then streams M once for more columns.  Chains too few for that (the scan of
+// then streams M once for more columns.  (128-column slices of 8 waves timed
+// no faster.)  Chains too few for that (the scan of
 // the group pairs) take 16 columns per workgroup, where the step latency of
 // few workgroups decides.
 hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream) {
