@@ -151,14 +151,25 @@ int64_t used_chunk_slots(int64_t T, int32_t N, const int32_t *cu_host) {
   }
   return 0;
 }
-size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
-  // sized for the most segments any plan over at most n_chunk_slots units can
-  // give (min(requested, units)), and for their groups (at most the group length)
+// Most segments any plan over at most n_chunk_slots units can give:
+// min(requested, units); and the most groups any of those segment counts gives
+// (taken over all of them, so that the buffers fit whatever the group length).
+int64_t max_split_segments(int64_t T, int32_t N, int64_t requested) {
   int64_t n_max = requested < 1 ? 1 : requested;
   if (n_max > kda::n_chunk_slots(T, N)) n_max = kda::n_chunk_slots(T, N);
+  return n_max;
+}
+int64_t max_scan_groups(int64_t n_max) {
+  int64_t m = 1;
+  for (int64_t n = 1; n <= n_max; ++n)
+    if (scan_groups(n) > m) m = scan_groups(n);
+  return m;
+}
+size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
+  const int64_t n_max = max_split_segments(T, N, requested);
   // chunk images, segment pairs [., D, 2D], group pairs and group entry states
   return kda::split_workspace_bytes(T, N, H) + (size_t)n_max * H * kD * 2 * kD * sizeof(float) +
-         scan_workspace(scan_group_len(n_max), H);
+         scan_workspace(max_scan_groups(n_max), H);
 }
 
 }  // namespace
@@ -325,10 +336,15 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (!workspace || workspace_bytes < need)
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    float *pairs = (float *)((char *)workspace + kda::split_workspace_bytes(T, N, H));
+    // the buffers are laid out for the largest plan the workspace size allows for
+    const int64_t n_max = max_split_segments(T, N, req), g_max = max_scan_groups(n_max);
     const int64_t glen = scan_group_len(sp.n_seg), n_groups = scan_groups(sp.n_seg);
-    float *gpairs = pairs + (size_t)sp.n_seg * H * kD * 2 * kD;
-    float *gentry = gpairs + (size_t)n_groups * H * kD * 2 * kD;
+    if (sp.n_seg > n_max || n_groups > g_max)
+      return fail(KDA_ERR_UNSUPPORTED, "segment plan exceeds its workspace layout (%lld segments, %lld groups)",
+                  (long long)sp.n_seg, (long long)n_groups);
+    float *pairs = (float *)((char *)workspace + kda::split_workspace_bytes(T, N, H));
+    float *gpairs = pairs + (size_t)n_max * H * kD * 2 * kD;
+    float *gentry = gpairs + (size_t)g_max * H * kD * 2 * kD;
 
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
                                       cu_seqlens, N, T, H, o, final_state, workspace);
