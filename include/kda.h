@@ -136,6 +136,35 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
                          size_t workspace_bytes, void *o, float *final_state, void *stream);
 
 /* ------------------------------------------------------------------------- */
+/* kda_chunk_fwd_checkpoints -- prefill that also emits the fp32 state inside
+ * every document every `interval` tokens, for a prefix cache (the systems
+ * page, section "KDA：三种执行形态" on prefill checkpoints; the recurrence holds
+ * the state at each chunk boundary, so these are extra stores).
+ *
+ * Same operator and arguments as kda_chunk_fwd on its two-kernel path (bf16
+ * inputs and arithmetic, workspace of kda_chunk_fwd_workspace_size bytes).
+ * interval: tokens, a positive multiple of 64.  For document d and every
+ * j >= 1 with j * interval < its length, the state after its first
+ * j * interval tokens (of shape [H, dk, dv], row = key channel) is written to
+ *   checkpoints[(floor(cu[d] / 64) + d + j * interval / 64 - 1) / (interval / 64)]
+ * (entries of other indices are not written; the state after a document's last
+ * token is final_state).  checkpoints: device memory of at least
+ * kda_checkpoint_count(N, T, interval) * H * dk * dv * 4 bytes.
+ * Errors: as kda_chunk_fwd; KDA_ERR_SHAPE for a bad interval, KDA_ERR_NULL for
+ * a NULL checkpoint buffer, KDA_ERR_WORKSPACE for a short one,
+ * KDA_ERR_UNSUPPORTED for fp32 inputs. */
+size_t kda_checkpoint_count(int32_t N, int64_t T, int32_t interval);
+
+int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const void *g_logits,
+                              const void *beta, const float *A_log, float g_min,
+                              const float *initial_state, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                              int32_t dk, int32_t dv, int32_t dtype, int32_t interval,
+                              float *checkpoints, size_t checkpoint_bytes, void *o,
+                              float *final_state, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* ------------------------------------------------------------------------- */
 /* kda_segment_scan -- intra-device context parallelism for long prefill.
  *
  * Same operator and arguments as kda_chunk_fwd.  The packed sequence is cut into

@@ -27,7 +27,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTY
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_prep",
-           "kda_chunk_recurrence", "kda_segment_scan",
+           "kda_chunk_recurrence", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count",
+           "kda_segment_scan",
            "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_status_string", "kda_last_error")
 
@@ -57,6 +58,11 @@ def load_library(path: str = LIB_PATH):
     prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_checkpoints.argtypes = prefill[:-1] + [i32, vp, ctypes.c_size_t, vp, vp, vp,
+                                                             ctypes.c_size_t, vp]
+    lib.kda_chunk_fwd_checkpoints.restype = ctypes.c_int
+    lib.kda_checkpoint_count.argtypes = [i32, i64, i32]
+    lib.kda_checkpoint_count.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32]
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, i32, i64, i32, i32, i32, i32,
@@ -192,6 +198,50 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                            ws_ptr, ws_bytes, _stream())
     _check(rc)
     return o, final_state
+
+
+def kda_checkpoint_count(N: int, T: int, interval: int) -> int:
+    return int(load_library().kda_checkpoint_count(N, T, interval))
+
+
+def checkpoint_index(cu_seqlens_host, d: int, j: int, interval: int) -> int:
+    """Index in the checkpoint array of the state after the first j * interval
+    tokens of document d (j >= 1, j * interval < the document's length)."""
+    cpi = interval // 64
+    first = int(cu_seqlens_host[d]) // 64 + d if cu_seqlens_host is not None else 0
+    return (first + j * cpi - 1) // cpi
+
+
+def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None,
+                              g_min: float = -5.0, initial_state=None, cu_seqlens=None,
+                              cu_seqlens_host=None, output_final_state: bool = True, o=None,
+                              final_state=None, checkpoints=None, workspace=None):
+    """kda_chunk_fwd (two-kernel path, bf16) that also writes the state every
+    ``interval`` tokens inside each document (see ``checkpoint_index``).
+    Returns (o, final_state, checkpoints [kda_checkpoint_count, H, 128, 128] fp32)."""
+    torch = _torch()
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
+                                                       initial_state, cu_seqlens, cu_seqlens_host)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if checkpoints is None:
+        n = kda_checkpoint_count(N, T, interval)
+        checkpoints = torch.empty((max(n, 1), H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
+                                device=q.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.kda_chunk_fwd_checkpoints(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log), float(g_min),
+        _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H, dk, dv, _dtype_code(q),
+        int(interval), _ptr(checkpoints), checkpoints.numel() * checkpoints.element_size(),
+        _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream())
+    _check(rc)
+    return o, final_state, checkpoints
 
 
 def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -5.0,

@@ -29,6 +29,7 @@ int hip_fail(hipError_t e, const char *what) {
 }
 
 constexpr int kD = 128;
+constexpr int kC = 64;  // chunk length
 
 // Sizes, dtype and document offsets shared by the prefill entry points.
 int check_layout(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N, int64_t T,
@@ -229,6 +230,48 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
     hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd empty documents");
+  }
+  return KDA_OK;
+}
+
+size_t kda_checkpoint_count(int32_t N, int64_t T, int32_t interval) {
+  if (N <= 0 || T < 0 || interval <= 0 || interval % kC != 0) return 0;
+  return (size_t)((kda::n_chunk_slots(T, N) - 1) / (interval / kC) + 1);
+}
+
+int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const void *g_logits,
+                              const void *beta, const float *A_log, float g_min,
+                              const float *initial_state, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                              int32_t dk, int32_t dv, int32_t dtype, int32_t interval,
+                              float *checkpoints, size_t checkpoint_bytes, void *o,
+                              float *final_state, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
+                         dk, dv, dtype, KDA_COMPUTE_AUTO, o);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "checkpoints are written by the bf16 two-kernel path only");
+  if (interval <= 0 || interval % kC != 0)
+    return fail(KDA_ERR_SHAPE, "checkpoint interval must be a positive multiple of %d tokens (got %d)", kC, interval);
+  if (!checkpoints) return fail(KDA_ERR_NULL, "checkpoints must be non-NULL");
+  const size_t need_ckpt = kda_checkpoint_count(N, T, interval) * (size_t)H * kD * kD * sizeof(float);
+  if (checkpoint_bytes < need_ckpt)
+    return fail(KDA_ERR_WORKSPACE, "checkpoint buffer of %zu bytes required (got %zu)", need_ckpt, checkpoint_bytes);
+  rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+  if (rc != KDA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
+                                      cu_seqlens, N, T, H, o, final_state, workspace);
+    p.ckpt = checkpoints;
+    p.ckpt_chunks = interval / kC;
+    hipError_t e = kda::launch_chunk_prep(p, st);
+    if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_checkpoints launch");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_checkpoints empty documents");
   }
   return KDA_OK;
 }

@@ -64,6 +64,10 @@ struct SplitParams {
   int64_t seg_slots;
   const float *entry;      // mode 1: entry state per segment [n_seg, H, D, D]
   float *pairs;            // mode 2: [n_seg, H, D, 2D], columns 0..127 S~, 128..255 M
+  // modes 0 and 1: the state after every ckpt_chunks-th chunk of a document
+  // (not after its last chunk) to ckpt[slot / ckpt_chunks, H, D, D]; 0 = none
+  float *ckpt;
+  int ckpt_chunks;
 };
 size_t split_workspace_bytes(int64_t T, int N, int H);
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);

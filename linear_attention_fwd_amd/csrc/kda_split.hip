@@ -389,10 +389,12 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][
   }
 }
 
-// The chunk a slot holds: document d, first token cs, len tokens (0: no chunk
-// maps to the slot), whether it starts and whether it ends its document.
+// The chunk a slot holds: document d, its index k in the document, first token
+// cs, len tokens (0: no chunk maps to the slot), whether it starts and whether
+// it ends its document.
 struct SlotChunk {
   int d;
+  int64_t k;
   int64_t cs;
   int len;
   bool first, last;
@@ -402,7 +404,8 @@ __device__ __forceinline__ SlotChunk slot_chunk(const SplitParams &p, int64_t sl
   c.d = doc_of_slot(p.cu, p.N, slot);
   const int64_t a = uni64(cu_at(p.cu, p.T, c.d));
   const int64_t b = uni64(cu_at(p.cu, p.T, c.d + 1));
-  c.cs = a + (slot - first_slot(a, c.d)) * CH;
+  c.k = slot - first_slot(a, c.d);
+  c.cs = a + c.k * CH;
   c.len = c.cs < b ? (int)min((int64_t)CH, b - c.cs) : 0;
   c.first = c.cs == a;
   c.last = c.cs + c.len == b;
@@ -628,6 +631,14 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
     }
     if (c.last && p.rmode != 2 && p.final_state) {
       float *f = uniptr(p.final_state + ((int64_t)c.d * H + h) * (D * D));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) state_store(S[t], f, D, colW + 16 * t, g, j);
+    }
+    // Checkpoints inside a document are ckpt_chunks or more slots apart (a later
+    // document's first one lies ckpt_chunks - 1 slots past its first slot), so
+    // slot / ckpt_chunks numbers them without collisions.
+    if (p.ckpt_chunks > 0 && p.rmode != 2 && !c.last && (c.k + 1) % p.ckpt_chunks == 0) {
+      float *f = uniptr(p.ckpt + ((sl / p.ckpt_chunks) * H + h) * (D * D));
 #pragma unroll
       for (int t = 0; t < NT; ++t) state_store(S[t], f, D, colW + 16 * t, g, j);
     }

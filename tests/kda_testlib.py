@@ -122,3 +122,23 @@ def gpu_decode(inp, t=None, state_slots=None, err_flag=None):
                             t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(t["state"])
+
+
+def oracle_checkpoints(inp, interval):
+    """{(d, j): state after the first j * interval tokens of document d [H, dk, dv]}
+    for every j >= 1 with j * interval < the document's length: the oracle's final
+    state over that prefix of the document."""
+    g_all = oracle.gate(inp.z.f64(), inp.A_log, inp.g_min)
+    cu = inp.cu_seqlens
+    out = {}
+    for d in range(inp.N):
+        a, b = int(cu[d]), int(cu[d + 1])
+        S0 = None if inp.S0 is None else inp.S0[d:d + 1].astype(np.float64)
+        j = 1
+        while j * interval < b - a:
+            e = a + j * interval
+            _, S = oracle.recurrent(inp.q.f64()[a:e], inp.k.f64()[a:e], inp.v.f64()[a:e],
+                                    g_all[a:e], inp.beta.f64()[a:e], S0)
+            out[(d, j)] = S[0]
+            j += 1
+    return out

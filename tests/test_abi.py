@@ -167,6 +167,35 @@ def test_prep_and_recurrence_validation(lib):
     assert rec(ws_bytes=0) == KDA_ERR_WORKSPACE
 
 
+def test_checkpoint_validation(lib):
+    # one entry per interval / 64 chunk slots: (floor(T / 64) + N - 1) // (interval / 64) + 1
+    assert lib.kda_checkpoint_count(1, 8192, 512) == (8192 // 64 + 1 - 1) // 8 + 1
+    assert lib.kda_checkpoint_count(3, 1000, 128) == (1000 // 64 + 3 - 1) // 2 + 1
+    assert lib.kda_checkpoint_count(1, 1000, 100) == 0      # not a multiple of 64
+    assert lib.kda_checkpoint_count(0, 1000, 128) == 0
+    ws = lib.kda_chunk_fwd_workspace_size(1, 128, 4, 128, 128)
+    nck = lib.kda_checkpoint_count(1, 128, 64) * 4 * 128 * 128 * 4
+
+    def call(**kw):
+        a = dict(q=FAKE, g_min=-5.0, N=1, T=128, H=4, dk=128, dtype=1, interval=64, ck=FAKE,
+                 ck_bytes=nck, o=FAKE, ws=FAKE, ws_bytes=ws)
+        a.update(kw)
+        return lib.kda_chunk_fwd_checkpoints(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["g_min"], None,
+                                             None, None, a["N"], a["T"], a["H"], a["dk"], 128,
+                                             a["dtype"], a["interval"], a["ck"], a["ck_bytes"],
+                                             a["o"], None, a["ws"], a["ws_bytes"], None)
+    assert call(q=None) == KDA_ERR_NULL
+    assert call(dk=64) == KDA_ERR_SHAPE
+    assert call(dtype=0) == KDA_ERR_UNSUPPORTED          # bf16 two-kernel path only
+    assert call(interval=0) == KDA_ERR_SHAPE
+    assert call(interval=96) == KDA_ERR_SHAPE
+    assert call(ck=None) == KDA_ERR_NULL
+    assert call(ck_bytes=nck - 1) == KDA_ERR_WORKSPACE
+    assert call(ws=None) == KDA_ERR_WORKSPACE
+    assert call(ws_bytes=ws - 1) == KDA_ERR_WORKSPACE
+    assert call(g_min=-6.0) == KDA_ERR_GATE_BOUND
+
+
 def test_decode_validation(lib):
     def call(**kw):
         a = dict(state=FAKE, slots=None, c=FAKE, acc=FAKE, W=4, n=FAKE, A=None, g_min=-5.0,

@@ -168,6 +168,74 @@ def test_segment_scan_many_segments_wide_recurrence():
     _check_prefill(inp, o, S, _tols(inp, 0))
 
 
+CHECKPOINT_CASES = {
+    # name: (generator kwargs, interval in tokens)
+    "varlen_128": (dict(seed=47, T=2300, H=3, dtype="bf16", lengths=[700, 0, 129, 1024, 383, 64],
+                        s0_std=0.02, s0_docs="all"), 128),
+    "single_doc_512": (dict(seed=48, T=2048, H=2, dtype="bf16", z_mean=-6.0, s0_std=0.05,
+                            s0_docs="all"), 512),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHECKPOINT_CASES))
+def test_checkpoints_match_oracle(name):
+    """States emitted every `interval` tokens inside each document equal the
+    oracle's state after that prefix; O and the final states are those of
+    kda_chunk_fwd, bit for bit."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    from kda_testlib import gpu_inputs, oracle_checkpoints
+    kw, interval = CHECKPOINT_CASES[name]
+    kw = dict(kw)
+    seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
+    inp = kda_gen.make_prefill(seed, T, H, **kw)
+    _case(inp, 0)
+    print(f"    checkpoint interval {interval}", flush=True)
+    t = gpu_inputs(inp)
+    o1, S1 = gpu_chunk_fwd(inp, t=t)
+    o2, S2, ck = kda.kda_chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["z"], t["beta"], interval,
+                                               t["A_log"], inp.g_min, t["S0"], t["cu"], t["cu_host"])
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, kda_gen.from_torch(o2)) and np.array_equal(S1, kda_gen.from_torch(S2))
+    ck = kda_gen.from_torch(ck)
+    ref = oracle_checkpoints(inp, interval)
+    assert ref, "the case must have checkpoints"
+    worst = 0.0
+    for (d, j), S_ref in ref.items():
+        i = kda.checkpoint_index(inp.cu_seqlens, d, j, interval)
+        for hh in range(inp.H):
+            e = np.linalg.norm(ck[i, hh] - S_ref[hh]) / np.linalg.norm(S_ref[hh])
+            worst = max(worst, e)
+    print(f"    {len(ref)} checkpoints, max rel L2 {worst:.3e}", flush=True)
+    assert worst <= TOL_BF16, worst
+
+
+def test_checkpoints_wide_recurrence():
+    """Checkpoints from the 128-column recurrence (enough documents to fill the
+    device)."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    from kda_testlib import gpu_inputs, oracle_checkpoints
+    rng = np.random.default_rng(49)
+    lengths = [int(x) for x in rng.integers(0, 400, size=36)]
+    interval = 192
+    inp = kda_gen.make_prefill(49, int(sum(lengths)), 8, "bf16", lengths=lengths, s0_std=0.02,
+                               s0_docs="all")
+    _case(inp, 0)
+    _units_fill_device(inp.N * inp.H)
+    t = gpu_inputs(inp)
+    o, S, ck = kda.kda_chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["z"], t["beta"], interval,
+                                             t["A_log"], inp.g_min, t["S0"], t["cu"], t["cu_host"])
+    torch.cuda.synchronize()
+    _check_prefill(inp, kda_gen.from_torch(o), kda_gen.from_torch(S), _tols(inp, 0))
+    ck = kda_gen.from_torch(ck)
+    ref = oracle_checkpoints(inp, interval)
+    worst = max(np.linalg.norm(ck[kda.checkpoint_index(inp.cu_seqlens, d, j, interval), hh] - S_ref[hh])
+                / np.linalg.norm(S_ref[hh]) for (d, j), S_ref in ref.items() for hh in range(inp.H))
+    print(f"    {len(ref)} checkpoints, max rel L2 {worst:.3e}", flush=True)
+    assert worst <= TOL_BF16, worst
+
+
 SCAN_CASES = {
     # lengths chosen so that segment boundaries fall inside documents, exactly on
     # a document start (n_seg=7 -> segments of 215 tokens; a document starts at 430),
