@@ -216,6 +216,13 @@ class DecodeInputs:
     W: int
     g_min: float = G_MIN
     dtype: str = "bf16"
+    # drafts of the next window, run after the bonus token (outputs only)
+    wq: Optional[Tensor] = None   # [N, W2, H, D]
+    wk: Optional[Tensor] = None
+    wv: Optional[Tensor] = None
+    wz: Optional[Tensor] = None
+    wbeta: Optional[Tensor] = None  # [N, W2, H]
+    W2: int = 0
 
     @property
     def N(self) -> int:
@@ -228,9 +235,11 @@ class DecodeInputs:
 
 def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
                 A_std: float = 0.5, s_std: float = 0.02, d: int = D,
-                accepted=None) -> DecodeInputs:
+                accepted=None, W2: int = 0) -> DecodeInputs:
     """Decode-with-verify recipe: draft cache first (q,k,v,z,beta order), then A,
-    the saved state, the accepted lengths U{0..W}, then the bonus token."""
+    the saved state, the accepted lengths U{0..W}, then the bonus token, then (if
+    W2 > 0) the W2 drafts of the next window.  The draws of a call with W2 > 0
+    start with exactly those of the same call with W2 = 0."""
     rng = np.random.default_rng(seed)
     T = N * W
     q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype)
@@ -248,8 +257,17 @@ def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
         acc = np.asarray(accepted, dtype=np.int32)
         assert acc.shape == (N,)
     nq, nk, nv, nz, nb = _draw_qkvzb(rng, N, H, d, dtype)
+    win = {}
+    if W2 > 0:
+        wq, wk, wv, wz, wb = _draw_qkvzb(rng, N * W2, H, d, dtype)
+        win = dict(wq=Tensor(wq.data.reshape(N, W2, H, d), dtype),
+                   wk=Tensor(wk.data.reshape(N, W2, H, d), dtype),
+                   wv=Tensor(wv.data.reshape(N, W2, H, d), dtype),
+                   wz=Tensor(wz.data.reshape(N, W2, H, d), dtype),
+                   wbeta=Tensor(wb.data.reshape(N, W2, H), dtype), W2=W2)
     return DecodeInputs(state=state, cq=cq, ck=ck, cv=cv, cz=cz, cbeta=cb, accepted=acc,
-                        nq=nq, nk=nk, nv=nv, nz=nz, nbeta=nb, A_log=A_log, W=W, dtype=dtype)
+                        nq=nq, nk=nk, nv=nv, nz=nz, nbeta=nb, A_log=A_log, W=W, dtype=dtype,
+                        **win)
 
 
 # ----------------------------------------------------------------------------

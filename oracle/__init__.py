@@ -154,3 +154,40 @@ def decode(inp, nthreads: int = 0):
     o, S = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
     o_bonus = o[cu[1:] - 1]
     return o_bonus, S
+
+
+def decode_window(inp, nthreads: int = 0):
+    """Decode step followed by the next draft window, on a ``kda_gen.DecodeInputs``
+    with W2 > 0 (the systems page, section "KDA：三种执行形态" on decode: replay,
+    bonus token and the next drafts in one loop).
+
+    The tokens of sequence n are its accepted drafts, the bonus token, then its W2
+    window drafts, run by the recurrence from the saved state.  Returns (o of the
+    bonus token [N,H,dv], o of the window drafts [N,W2,H,dv], the state after the
+    bonus token [N,H,dk,dv], the one that is kept: the window's drafts are not yet
+    verified)."""
+    N, W, H, d = inp.cq.shape
+    W2 = inp.W2
+    acc = np.clip(inp.accepted.astype(np.int64), 0, W)
+    lens = acc + 1 + W2
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    q = np.empty((T, H, d)); k = np.empty((T, H, d)); v = np.empty((T, H, d))
+    z = np.empty((T, H, d)); b = np.empty((T, H))
+    parts = [(inp.cq.f64(), inp.ck.f64(), inp.cv.f64(), inp.cz.f64(), inp.cbeta.f64()),
+             (inp.nq.f64()[:, None], inp.nk.f64()[:, None], inp.nv.f64()[:, None],
+              inp.nz.f64()[:, None], inp.nbeta.f64()[:, None]),
+             (inp.wq.f64(), inp.wk.f64(), inp.wv.f64(), inp.wz.f64(), inp.wbeta.f64())]
+    for n in range(N):
+        s = int(cu[n])
+        for (pq, pk, pv, pz, pb), m in zip(parts, (int(acc[n]), 1, W2)):
+            q[s:s + m], k[s:s + m], v[s:s + m], z[s:s + m], b[s:s + m] = (
+                pq[n, :m], pk[n, :m], pv[n, :m], pz[n, :m], pb[n, :m])
+            s += m
+    g = gate(z, inp.A_log, inp.g_min)
+    o, _ = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
+    o_bonus = o[cu[:-1] + acc]
+    o_window = np.stack([o[cu[n] + acc[n] + 1:cu[n + 1]] for n in range(N)])
+    _, S = decode(inp, nthreads)
+    return o_bonus, o_window, S

@@ -274,6 +274,42 @@ def test_decode_replay_equals_explicit_steps(oracle_mod):
             assert _rel(S[n, h], Sb) < 1e-12
 
 
+def test_decode_window_equals_explicit_steps(oracle_mod):
+    """Replay, bonus token and the next draft window in one loop (systems page,
+    decode): the window drafts' outputs are eq. (1) stepped explicitly past the
+    bonus token, and the state kept is the one after the bonus token, whatever
+    the window holds."""
+    inp = kda_gen.make_decode(12, N=5, H=2, W=4, dtype="bf16", d=128,
+                              accepted=[0, 4, 1, 3, 2], W2=3)
+    o, ow, S = oracle_mod.decode_window(inp)
+    assert ow.shape == (inp.N, 3, inp.H, 128)
+    gate = lambda z: oracle_mod.gate(z[None, None, :], inp.A_log[None, h:h + 1], inp.g_min)[0, 0]
+    cat = lambda c, b, w, n, a, h: np.concatenate([c.f64()[n, :a, h], b.f64()[n, None, h],
+                                                    w.f64()[n, :, h]])
+    for n in range(inp.N):
+        a = int(inp.accepted[n])
+        for h in range(inp.H):
+            qs = cat(inp.cq, inp.nq, inp.wq, n, a, h)
+            ks = cat(inp.ck, inp.nk, inp.wk, n, a, h)
+            vs = cat(inp.cv, inp.nv, inp.wv, n, a, h)
+            zs = cat(inp.cz, inp.nz, inp.wz, n, a, h)
+            bs = cat(inp.cbeta, inp.nbeta, inp.wbeta, n, a, h)
+            gs = np.stack([gate(z) for z in zs])
+            S0 = inp.state[n, h].astype(np.float64)
+            ob, _ = brute.run(qs, ks, vs, gs, bs, S0)
+            _, Sb = brute.run(qs[:a + 1], ks[:a + 1], vs[:a + 1], gs[:a + 1], bs[:a + 1], S0)
+            assert _rel(o[n, h], ob[a]) < 1e-12
+            for j in range(3):
+                assert _rel(ow[n, j, h], ob[a + 1 + j]) < 1e-12
+            assert _rel(S[n, h], Sb) < 1e-12
+    # the bonus output and kept state do not depend on the window
+    o0, S0_ = oracle_mod.decode(inp)
+    assert np.array_equal(o0, o) and np.array_equal(S0_, S)
+    # the window's draws come after those of the plain recipe
+    plain = kda_gen.make_decode(12, N=5, H=2, W=4, dtype="bf16", d=128, accepted=[0, 4, 1, 3, 2])
+    assert np.array_equal(plain.state, inp.state) and np.array_equal(plain.nq.data, inp.nq.data)
+
+
 # ---------------------------------------------------------------------------
 # Cost models printed on the SemiAnalysis page ("复杂度分析") and the KCP volume
 # ---------------------------------------------------------------------------
