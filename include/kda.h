@@ -234,6 +234,34 @@ int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, co
                     float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
                     int32_t dv, int32_t dtype, void *stream);
 
+/* kda_decode_step_window -- kda_decode_step fused with the next draft window.
+ *
+ * The same step as kda_decode_step (same arguments, same state written, same o
+ * for the bonus token), followed in the same recurrence loop by W2 tokens of
+ * the next draft window: each advances the on-chip state by one recurrence step
+ * and produces its output, but no state after the bonus token is written (the
+ * window's drafts are verified by the following step, which replays the ones
+ * accepted from their cached inputs).  This is the loop of the systems page,
+ * section "KDA：三种执行形态" (decode: replay, bonus token and the next draft
+ * window in one kernel), on the recurrence of the SemiAnalysis page, section
+ * "FlashKDA 算法".
+ *
+ *   wq, wk, wv, wz  [N, W2, H, 128] dtype  next-window draft inputs
+ *   wbeta        [N, W2, H] dtype
+ *   W2           >= 0; with W2 = 0 the window pointers may be NULL and the call
+ *                equals kda_decode_step
+ *   o_window     [N, W2, H, 128] dtype (written): output of each window draft
+ * Errors as for kda_decode_step; KDA_ERR_NULL when W2 > 0 and a window pointer
+ * is NULL. */
+int kda_decode_step_window(float *state, const int32_t *state_slots, const void *cq,
+                           const void *ck, const void *cv, const void *cz, const void *cbeta,
+                           const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                           const void *nv, const void *nz, const void *nbeta, const void *wq,
+                           const void *wk, const void *wv, const void *wz, const void *wbeta,
+                           int32_t W2, const float *A_log, float g_min, void *o, void *o_window,
+                           int32_t *err_flag, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                           int32_t dtype, void *stream);
+
 /* ------------------------------------------------------------------------- */
 const char *kda_status_string(int status);  /* static string */
 const char *kda_last_error(void);           /* thread-local detail of the last failure */

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
   * ``kda_chunk_fwd``    -- chunkwise prefill of packed documents
   * ``kda_segment_scan`` -- prefill with intra-device segment pairs + scan
   * ``kda_decode_step``  -- decode step with speculative-verify replay
+  * ``kda_decode_step_window`` -- the same step fused with the next draft window
 """
 from __future__ import annotations
 
@@ -30,7 +31,8 @@ EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_prep",
            "kda_chunk_recurrence", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count",
            "kda_segment_scan",
            "kda_segment_scan_workspace_size",
-           "kda_default_segments", "kda_decode_step", "kda_status_string", "kda_last_error")
+           "kda_default_segments", "kda_decode_step", "kda_decode_step_window", "kda_status_string",
+           "kda_last_error")
 
 _lib = None
 
@@ -80,6 +82,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                     f32, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, i32, vp, f32, vp, vp, vp, i32, i32,
+                                           i32, i32, i32, vp]
+    lib.kda_decode_step_window.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -356,6 +362,50 @@ def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbet
     return o
 
 
+def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
+                           wq, wk, wv, wz, wbeta, A_log=None, g_min: float = -5.0,
+                           state_slots=None, o=None, o_window=None, err_flag=None):
+    """``kda_decode_step`` followed, in the same kernel, by the next draft window.
+
+    Arguments as for ``kda_decode_step`` plus wq, wk, wv, wz: [N, W2, H, 128] and
+    wbeta: [N, W2, H], the drafts of the next window.  ``state`` receives the state
+    after the bonus token, as with ``kda_decode_step``.  Returns (o, o_window):
+    o [N, H, 128] for the bonus token, o_window [N, W2, H, 128] for the drafts."""
+    torch = _torch()
+    lib = load_library()
+    _dev(state, "state", torch.float32)
+    N, H, d = nq.shape
+    W = cq.shape[1] if cq is not None else 0
+    W2 = wq.shape[1]
+    dt = nq.dtype
+    for name, t in (("cq", cq), ("ck", ck), ("cv", cv), ("cz", cz), ("cbeta", cbeta), ("nq", nq),
+                    ("nk", nk), ("nv", nv), ("nz", nz), ("nbeta", nbeta), ("wq", wq), ("wk", wk),
+                    ("wv", wv), ("wz", wz), ("wbeta", wbeta)):
+        _dev(t, name, dt)
+    for name, t in (("wk", wk), ("wv", wv), ("wz", wz)):
+        if tuple(t.shape) != tuple(wq.shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(wq.shape)}")
+    if tuple(wq.shape) != (N, W2, H, d) or tuple(wbeta.shape) != (N, W2, H):
+        raise ValueError("next-window inputs must be [N, W2, H, 128] and [N, W2, H]")
+    _dev(accepted, "accepted", torch.int32)
+    _dev(state_slots, "state_slots", torch.int32)
+    _dev(A_log, "A_log", torch.float32)
+    _dev(err_flag, "err_flag", torch.int32)
+    if o is None:
+        o = torch.empty((N, H, d), dtype=dt, device=nq.device)
+    if o_window is None:
+        o_window = torch.empty((N, W2, H, d), dtype=dt, device=nq.device)
+    _dev(o_window, "o_window", dt)
+    rc = lib.kda_decode_step_window(
+        _ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
+        _ptr(accepted), int(W), _ptr(nq), _ptr(nk), _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(wq),
+        _ptr(wk), _ptr(wv), _ptr(wz), _ptr(wbeta), int(W2), _ptr(A_log), float(g_min), _ptr(o),
+        _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq), _stream())
+    _check(rc)
+    return o, o_window
+
+
 __all__ = ["kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
-           "kda_default_segments", "kda_decode_step", "load_library", "KDAError",
+           "kda_default_segments", "kda_decode_step", "kda_decode_step_window",
+           "kda_chunk_fwd_checkpoints", "kda_checkpoint_count", "load_library", "KDAError",
            "KDA_COMPUTE_AUTO", "KDA_COMPUTE_F32"]

@@ -471,14 +471,16 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   return KDA_OK;
 }
 
-int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
-                    const void *cv, const void *cz, const void *cbeta,
-                    const int32_t *accepted, int32_t W, const void *nq, const void *nk,
-                    const void *nv, const void *nz, const void *nbeta, const float *A_log,
-                    float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
-                    int32_t dv, int32_t dtype, void *stream) {
+static int decode_common(float *state, const int32_t *state_slots, const void *cq,
+                         const void *ck, const void *cv, const void *cz, const void *cbeta,
+                         const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                         const void *nv, const void *nz, const void *nbeta,
+                         const kda::DecodeWindowArgs &win, const float *A_log, float g_min,
+                         void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
+                         int32_t dv, int32_t dtype, void *stream, const char *who) {
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
-  if (N < 0 || H <= 0 || W < 0) return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0");
+  if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
+    return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");
   if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "N * H too large");
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (!(g_min >= -5.0f && g_min < 0.0f))
@@ -488,14 +490,42 @@ int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, co
     return fail(KDA_ERR_NULL, "state, accepted, bonus inputs and o must be non-NULL");
   if (W > 0 && (!cq || !ck || !cv || !cz || !cbeta))
     return fail(KDA_ERR_NULL, "draft caches must be non-NULL when W > 0");
+  if (win.W2 > 0 && (!win.q || !win.k || !win.v || !win.z || !win.beta || !win.o))
+    return fail(KDA_ERR_NULL, "next-window inputs and outputs must be non-NULL when W2 > 0");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = (dtype == KDA_BF16)
       ? kda::launch_decode<kda::bf16_t>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq,
-                                        nk, nv, nz, nbeta, A_log, g_min, o, err_flag, N, H, st)
+                                        nk, nv, nz, nbeta, win, A_log, g_min, o, err_flag, N, H, st)
       : kda::launch_decode<float>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk,
-                                  nv, nz, nbeta, A_log, g_min, o, err_flag, N, H, st);
-  if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+                                  nv, nz, nbeta, win, A_log, g_min, o, err_flag, N, H, st);
+  if (e != hipSuccess) return hip_fail(e, who);
   return KDA_OK;
+}
+
+int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
+                    const void *cv, const void *cz, const void *cbeta,
+                    const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                    const void *nv, const void *nz, const void *nbeta, const float *A_log,
+                    float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
+                    int32_t dv, int32_t dtype, void *stream) {
+  const kda::DecodeWindowArgs none{0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return decode_common(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv, nz,
+                       nbeta, none, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
+                       "kda_decode_step launch");
+}
+
+int kda_decode_step_window(float *state, const int32_t *state_slots, const void *cq,
+                           const void *ck, const void *cv, const void *cz, const void *cbeta,
+                           const int32_t *accepted, int32_t W, const void *nq, const void *nk,
+                           const void *nv, const void *nz, const void *nbeta, const void *wq,
+                           const void *wk, const void *wv, const void *wz, const void *wbeta,
+                           int32_t W2, const float *A_log, float g_min, void *o, void *o_window,
+                           int32_t *err_flag, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                           int32_t dtype, void *stream) {
+  const kda::DecodeWindowArgs win{W2, wq, wk, wv, wz, wbeta, o_window};
+  return decode_common(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv, nz,
+                       nbeta, win, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
+                       "kda_decode_step_window launch");
 }
 
 }  // extern "C"

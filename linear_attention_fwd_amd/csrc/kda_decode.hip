@@ -24,6 +24,14 @@
 namespace kda {
 
 constexpr int DEC_THREADS = 256;
+
+// The drafts of the next window: inputs [N, W2, H, D] (beta [N, W2, H]) and
+// their outputs o [N, W2, H, D]; W2 = 0 means none.
+template <typename Tin> struct DecodeWindow {
+  int W2;
+  const Tin *q, *k, *v, *z, *beta;
+  Tin *o;
+};
 constexpr int DEC_TOKBATCH = 8;  // tokens staged in LDS at a time
 
 template <typename Tin>
@@ -34,8 +42,9 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                   const Tin *__restrict__ cbeta, const int32_t *__restrict__ accepted, int W,
                   const Tin *__restrict__ nq, const Tin *__restrict__ nk,
                   const Tin *__restrict__ nv, const Tin *__restrict__ nz,
-                  const Tin *__restrict__ nbeta, const float *__restrict__ A_log, float g_min,
-                  Tin *__restrict__ o, int32_t *__restrict__ err_flag, int H) {
+                  const Tin *__restrict__ nbeta, DecodeWindow<Tin> win,
+                  const float *__restrict__ A_log, float g_min, Tin *__restrict__ o,
+                  int32_t *__restrict__ err_flag, int H) {
   __shared__ __align__(16) float s_k[DEC_TOKBATCH][D];
   __shared__ __align__(16) float s_q[DEC_TOKBATCH][D];
   __shared__ __align__(16) float s_a[DEC_TOKBATCH][D];
@@ -57,7 +66,9 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
     if (tid == 0 && err_flag) *err_flag = 1;
     acc = acc < 0 ? 0 : W;
   }
-  const int ntok = acc + 1;  // replayed drafts + bonus
+  // tokens: the acc accepted drafts (replayed), the bonus token, then the
+  // W2 drafts of the next window (outputs only; their states are not kept)
+  const int ntok = acc + 1 + win.W2;
   const int64_t slot = slots ? (int64_t)slots[n] : (int64_t)n;
   float *__restrict__ Sg = state + (slot * H + h) * (int64_t)(D * D);
 
@@ -74,7 +85,6 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
   }
 
   const float escale = __expf(A_log ? A_log[h] : 0.0f);
-  float ob[4] = {0.f, 0.f, 0.f, 0.f};
 
   for (int t0 = 0; t0 < ntok; t0 += DEC_TOKBATCH) {
     const int nb = min(DEC_TOKBATCH, ntok - t0);
@@ -86,9 +96,12 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
       if (t < acc) {
         const int64_t base = (((int64_t)n * W + t) * H + h) * D;
         pq = cq + base; pk = ck + base; pv = cv + base; pz = cz + base;
-      } else {
+      } else if (t == acc) {
         const int64_t base = ((int64_t)n * H + h) * D;
         pq = nq + base; pk = nk + base; pv = nv + base; pz = nz + base;
+      } else {
+        const int64_t base = (((int64_t)n * win.W2 + (t - acc - 1)) * H + h) * D;
+        pq = win.q + base; pk = win.k + base; pv = win.v + base; pz = win.z + base;
       }
       s_q[tt][c] = io<Tin>::load1(pq + c);
       s_k[tt][c] = io<Tin>::load1(pk + c);
@@ -97,13 +110,14 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
     }
     if (tid < nb) {
       const int t = t0 + tid;
-      s_b[tid] = (t < acc) ? io<Tin>::load1(cbeta + ((int64_t)n * W + t) * H + h)
-                           : io<Tin>::load1(nbeta + (int64_t)n * H + h);
+      s_b[tid] = (t < acc)    ? io<Tin>::load1(cbeta + ((int64_t)n * W + t) * H + h)
+                 : (t == acc) ? io<Tin>::load1(nbeta + (int64_t)n * H + h)
+                              : io<Tin>::load1(win.beta + ((int64_t)n * win.W2 + (t - acc - 1)) * H + h);
     }
     __syncthreads();
 
     for (int tt = 0; tt < nb; ++tt) {
-      const bool last = (t0 + tt == ntok - 1);
+      const int t = t0 + tt;
       float kk[16], aa[16];
 #pragma unroll
       for (int i = 0; i < 16; i += 4) {
@@ -140,8 +154,8 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
 #pragma unroll
         for (int c = 0; c < 4; ++c) s[i][c] = fmaf(kk[i], u[c], s[i][c]);
       }
-      if (last) {
-        float qq[16];
+      if (t >= acc) {  // the bonus token and the next window: o = S^T q
+        float qq[16], ob[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 16; i += 4) {
           const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][row0 + i]);
@@ -158,30 +172,37 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
           ob[c] += __shfl_xor(ob[c], 16);
           ob[c] += __shfl_xor(ob[c], 32);
         }
+        if (rg == 0) {
+          Tin *dst = (t == acc) ? o + ((int64_t)n * H + h) * D
+                                : win.o + (((int64_t)n * win.W2 + (t - acc - 1)) * H + h) * D;
+          io<Tin>::store4(dst + col0, ob);
+        }
+      }
+      if (t == acc) {  // the state after the bonus token is the one kept
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __builtin_nontemporal_store(floatx4{s[i][0], s[i][1], s[i][2], s[i][3]},
+                                      reinterpret_cast<floatx4 *>(Sg + (row0 + i) * D + col0));
       }
     }
     __syncthreads();  // the staging buffers are rewritten by the next batch
   }
-
-  if (rg == 0) io<Tin>::store4(o + ((int64_t)n * H + h) * D + col0, ob);
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    __builtin_nontemporal_store(floatx4{s[i][0], s[i][1], s[i][2], s[i][3]},
-                                reinterpret_cast<floatx4 *>(Sg + (row0 + i) * D + col0));
 }
 
 template <typename Tin>
 hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, const void *ck,
                          const void *cv, const void *cz, const void *cbeta,
                          const int32_t *accepted, int W, const void *nq, const void *nk,
-                         const void *nv, const void *nz, const void *nbeta, const float *A_log,
-                         float g_min, void *o, int32_t *err_flag, int N, int H,
-                         hipStream_t stream) {
+                         const void *nv, const void *nz, const void *nbeta,
+                         const DecodeWindowArgs &w, const float *A_log, float g_min, void *o,
+                         int32_t *err_flag, int N, int H, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)N * H));
+  DecodeWindow<Tin> win{w.W2, (const Tin *)w.q, (const Tin *)w.k, (const Tin *)w.v,
+                        (const Tin *)w.z, (const Tin *)w.beta, (Tin *)w.o};
   hipLaunchKernelGGL(kda_decode_kernel<Tin>, grid, dim3(DEC_THREADS), 0, stream, state, slots,
                      (const Tin *)cq, (const Tin *)ck, (const Tin *)cv, (const Tin *)cz,
                      (const Tin *)cbeta, accepted, W, (const Tin *)nq, (const Tin *)nk,
-                     (const Tin *)nv, (const Tin *)nz, (const Tin *)nbeta, A_log, g_min,
+                     (const Tin *)nv, (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min,
                      (Tin *)o, err_flag, H);
   return hipGetLastError();
 }
@@ -190,13 +211,13 @@ template hipError_t launch_decode<float>(float *, const int32_t *, const void *,
                                          const void *, const void *, const void *,
                                          const int32_t *, int, const void *, const void *,
                                          const void *, const void *, const void *,
-                                         const float *, float, void *, int32_t *, int, int,
-                                         hipStream_t);
+                                         const DecodeWindowArgs &, const float *, float, void *,
+                                         int32_t *, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(float *, const int32_t *, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const int32_t *, int, const void *, const void *,
                                           const void *, const void *, const void *,
-                                          const float *, float, void *, int32_t *, int, int,
-                                          hipStream_t);
+                                          const DecodeWindowArgs &, const float *, float, void *,
+                                          int32_t *, int, int, hipStream_t);
 
 }  // namespace kda

@@ -98,12 +98,21 @@ struct ScanChains {
 // n_cu: compute units of the device (chooses the columns per workgroup)
 hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream);
 
+// Drafts of the next window that a decode step runs after the bonus token
+// (outputs only): q, k, v, z [N, W2, H, D], beta [N, W2, H], o [N, W2, H, D];
+// W2 = 0 and null pointers when there is no window.
+struct DecodeWindowArgs {
+  int W2;
+  const void *q, *k, *v, *z, *beta;
+  void *o;
+};
+
 template <typename Tin>
 hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, const void *ck,
                          const void *cv, const void *cz, const void *cbeta,
                          const int32_t *accepted, int W, const void *nq, const void *nk,
-                         const void *nv, const void *nz, const void *nbeta, const float *A_log,
-                         float g_min, void *o, int32_t *err_flag, int N, int H,
-                         hipStream_t stream);
+                         const void *nv, const void *nz, const void *nbeta,
+                         const DecodeWindowArgs &win, const float *A_log, float g_min, void *o,
+                         int32_t *err_flag, int N, int H, hipStream_t stream);
 
 }  // namespace kda

@@ -107,6 +107,9 @@ def decode_gpu_inputs(inp, device="cuda"):
     import torch
     t = {name: kda_gen.to_torch(getattr(inp, name), device)
          for name in ("cq", "ck", "cv", "cz", "cbeta", "nq", "nk", "nv", "nz", "nbeta")}
+    if inp.W2 > 0:
+        for name in ("wq", "wk", "wv", "wz", "wbeta"):
+            t[name] = kda_gen.to_torch(getattr(inp, name), device)
     t["A_log"] = torch.from_numpy(inp.A_log).to(device)
     t["accepted"] = torch.from_numpy(inp.accepted).to(device)
     t["state"] = torch.from_numpy(inp.state).to(device)
@@ -122,6 +125,19 @@ def gpu_decode(inp, t=None, state_slots=None, err_flag=None):
                             t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(t["state"])
+
+
+def gpu_decode_window(inp, t=None, state_slots=None, err_flag=None):
+    """kda_decode_step_window on ``inp`` (W2 > 0): (o bonus, o window, state)."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    t = t or decode_gpu_inputs(inp)
+    o, ow = kda.kda_decode_step_window(
+        t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"], t["accepted"], t["nq"],
+        t["nk"], t["nv"], t["nz"], t["nbeta"], t["wq"], t["wk"], t["wv"], t["wz"], t["wbeta"],
+        t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
+    torch.cuda.synchronize()
+    return kda_gen.from_torch(o), kda_gen.from_torch(ow), kda_gen.from_torch(t["state"])
 
 
 def oracle_checkpoints(inp, interval):

@@ -218,6 +218,24 @@ def test_decode_validation(lib):
     assert lib.kda_last_error() is not None
 
 
+def test_decode_window_validation(lib):
+    def call(**kw):
+        a = dict(state=FAKE, c=FAKE, acc=FAKE, W=4, n=FAKE, w=FAKE, W2=4, o=FAKE, ow=FAKE,
+                 N=8, H=4, dtype=1)
+        a.update(kw)
+        c, n, w = a["c"], a["n"], a["w"]
+        return lib.kda_decode_step_window(a["state"], None, c, c, c, c, c, a["acc"], a["W"], n, n,
+                                          n, n, n, w, w, w, w, w, a["W2"], None, -5.0, a["o"],
+                                          a["ow"], None, a["N"], a["H"], 128, 128, a["dtype"],
+                                          None)
+    assert call(w=None) == KDA_ERR_NULL          # window inputs needed when W2 > 0
+    assert call(ow=None) == KDA_ERR_NULL
+    assert call(W2=-1) == KDA_ERR_SHAPE
+    assert call(dtype=5) == KDA_ERR_DTYPE
+    assert call(state=None) == KDA_ERR_NULL
+    assert call(N=0) == KDA_OK
+
+
 def test_one_hip_runtime_per_process():
     """Loading the library before torch has touched anything must not bring in a
     second HIP runtime (PyTorch ships its own; with two in one process the one

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import kda_gen
-from kda_testlib import (TOL_BF16, TOL_BF16_STORAGE, TOL_F32, gpu_chunk_fwd, gpu_decode, gpu_segment_scan,
+from kda_testlib import (TOL_BF16, TOL_BF16_STORAGE, TOL_F32, gpu_chunk_fwd, gpu_decode,
+                         gpu_decode_window, gpu_segment_scan,
                          decode_gpu_inputs, oracle_forward, rel_l2_slices)
 import oracle
 
@@ -314,6 +315,64 @@ def test_decode_slots_and_clamping():
     assert es <= TOL_F32 and eo <= TOL_BF16
     untouched = np.setdiff1d(np.arange(12), slots)
     assert np.all(P[untouched] == 0)
+
+
+@pytest.mark.parametrize("dtype,W2", [("bf16", 4), ("f32", 4), ("bf16", 13)])
+def test_decode_window_matches_oracle(dtype, W2):
+    """Replay + bonus + next draft window in one kernel: the bonus output and the
+    state kept equal those of kda_decode_step bit for bit (the same arithmetic on
+    the same tokens), and the window drafts' outputs match the oracle.  W2 = 13
+    runs the token loop past two staging batches."""
+    import torch
+    inp = kda_gen.make_decode(54, N=24, H=4, W=4, dtype=dtype,
+                              accepted=[i % 5 for i in range(24)], W2=W2)
+    print(f"[case] decode window N={inp.N} H={inp.H} W={inp.W} W2={W2} dtype={dtype}",
+          flush=True)
+    o_ref, ow_ref, S_ref = oracle.decode_window(inp)
+    o, ow, S = gpu_decode_window(inp)
+    o1, S1 = gpu_decode(inp)
+    assert np.array_equal(S, S1)
+    assert np.array_equal(o, o1)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    ew = max(rel_l2_slices(ow[:, j][:, :, None], ow_ref[:, j][:, :, None], axis_tokens=False)[0]
+             for j in range(W2))
+    print(f"    o: {eo:.3e}  window: {ew:.3e}  state: {es:.3e}", flush=True)
+    assert es <= TOL_F32
+    assert eo <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    assert ew <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def test_decode_window_slots_and_empty_window():
+    """Pool slots with the window; W2 = 0 is the plain decode step."""
+    import torch
+    import linear_attention_fwd_amd as kda
+    inp = kda_gen.make_decode(55, N=6, H=2, W=4, dtype="bf16", accepted=[0, 4, 1, 3, 2, 4], W2=2)
+    slots = np.array([7, 0, 3, 10, 5, 1], dtype=np.int32)
+    pool = np.zeros((11, inp.H, 128, 128), np.float32)
+    pool[slots] = inp.state
+    t = decode_gpu_inputs(inp)
+    t["state"] = torch.from_numpy(pool).cuda()
+    o, ow, P = gpu_decode_window(inp, t=t, state_slots=torch.from_numpy(slots).cuda())
+    o_ref, ow_ref, S_ref = oracle.decode_window(inp)
+    assert rel_l2_slices(P[slots], S_ref, axis_tokens=False)[0] <= TOL_F32
+    assert rel_l2_slices(ow.reshape(-1, inp.H, 128)[:, :, None],
+                         ow_ref.reshape(-1, inp.H, 128)[:, :, None], axis_tokens=False)[0] <= TOL_BF16
+    untouched = np.setdiff1d(np.arange(11), slots)
+    assert np.all(P[untouched] == 0)
+    # an empty window
+    t0 = decode_gpu_inputs(inp)
+    e = torch.empty((inp.N, 0, inp.H, 128), dtype=t0["wq"].dtype, device="cuda")
+    eb = torch.empty((inp.N, 0, inp.H), dtype=t0["wq"].dtype, device="cuda")
+    o0, ow0 = kda.kda_decode_step_window(
+        t0["state"], t0["cq"], t0["ck"], t0["cv"], t0["cz"], t0["cbeta"], t0["accepted"],
+        t0["nq"], t0["nk"], t0["nv"], t0["nz"], t0["nbeta"], e, e, e, e, eb, t0["A_log"],
+        inp.g_min)
+    torch.cuda.synchronize()
+    o1, S1 = gpu_decode(inp)
+    assert ow0.shape == (inp.N, 0, inp.H, 128)
+    assert np.array_equal(kda_gen.from_torch(o0), o1)
+    assert np.array_equal(kda_gen.from_torch(t0["state"]), S1)
 
 
 def test_decode_equals_chunk_fwd_on_the_same_tokens():
