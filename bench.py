@@ -260,10 +260,35 @@ def main():
     t_model = max(model_bytes / (HBM_PEAK_GBPS * 1e9), model_flops / (BF16_PEAK_TFLOPS * 1e12))
     step_kernel_ms = prep_ms + rec_ms
 
+    # ---------------- the same step with prefix-cache checkpoints -----------
+    interval = 512
+    n_ck = kda.kda_checkpoint_count(1, T, interval)
+    ck = torch.empty((n_ck, H, 128, 128), dtype=torch.float32, device=dev)
+
+    def ck_step():
+        kda.kda_chunk_fwd_checkpoints(q, k, v, z, b, interval, A_log, inp.g_min, o=o,
+                                      final_state=fin, checkpoints=ck, workspace=ws)
+
+    for _ in range(args.warmup):
+        ck_step()
+    torch.cuda.synchronize()
+    ck_ev = _events(torch, stream, args.steps)
+    for i in range(args.steps):
+        ck_ev[i][0].record(stream)
+        ck_step()
+        ck_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ck_ms = float(np.mean([a.elapsed_time(c) for a, c in ck_ev]))
+    ck_written = (T // interval - (1 if T % interval == 0 else 0)) * H * 128 * 128 * 4
+
     # ---------------- decode with speculative verify -------------------------
-    dec = kda_gen.workload(4)
+    # the decode workload (N=512, H=96, 4 drafts + bonus) plus, drawn after it, a
+    # next window of 4 drafts for the fused replay + bonus + window step
+    W2 = 4
+    dec = kda_gen.make_decode(4, 512, 96, 4, "bf16", W2=W2)
     dt = {n: kda_gen.to_torch(getattr(dec, n), dev)
-          for n in ("cq", "ck", "cv", "cz", "cbeta", "nq", "nk", "nv", "nz", "nbeta")}
+          for n in ("cq", "ck", "cv", "cz", "cbeta", "nq", "nk", "nv", "nz", "nbeta",
+                    "wq", "wk", "wv", "wz", "wbeta")}
     d_state = torch.from_numpy(dec.state).to(dev)
     d_acc = torch.from_numpy(dec.accepted).to(dev)
     d_A = torch.from_numpy(dec.A_log).to(dev)
@@ -286,6 +311,25 @@ def main():
     dec_ms = float(np.mean([a.elapsed_time(c) for a, c in dev_ev]))
     dec_bytes = decode_state_bytes(dec.N, dec.H)
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    d_ow = torch.empty((dec.N, W2, dec.H, 128), dtype=torch.bfloat16, device=dev)
+
+    def wstep():
+        kda.kda_decode_step_window(d_state, dt["cq"], dt["ck"], dt["cv"], dt["cz"], dt["cbeta"],
+                                   d_acc, dt["nq"], dt["nk"], dt["nv"], dt["nz"], dt["nbeta"],
+                                   dt["wq"], dt["wk"], dt["wv"], dt["wz"], dt["wbeta"], d_A,
+                                   dec.g_min, o=d_o, o_window=d_ow)
+
+    for _ in range(args.warmup):
+        wstep()
+    torch.cuda.synchronize()
+    win_ev = _events(torch, stream, args.decode_steps)
+    for i in range(args.decode_steps):
+        win_ev[i][0].record(stream)
+        wstep()
+        win_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    win_ms = float(np.mean([a.elapsed_time(c) for a, c in win_ev]))
 
     # ---------------- CPU oracle baseline (host cores of this machine) -----------
     cpu = None
@@ -336,9 +380,14 @@ def main():
                               "bytes": floor_bytes,
                               "GBps": floor_bytes / (step_kernel_ms * 1e-3) / 1e9,
                               "frac": floor_bytes / (step_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "checkpoints": {"interval_tokens": interval, "kernels_ms": ck_ms,
+                        "extra_ms": ck_ms - step_kernel_ms, "state_bytes_written": ck_written},
         "decode": {"workload": "N=512 H=96, 4 drafts + bonus, accepted U{0..4}, fp32 state",
                    "kernel_ms": dec_ms, "state_GBps": dec_gbps,
-                   "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS, "state_bytes": dec_bytes},
+                   "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS, "state_bytes": dec_bytes,
+                   "with_next_window": {"drafts": W2, "kernel_ms": win_ms,
+                                        "extra_ms": win_ms - dec_ms,
+                                        "state_GBps": dec_bytes / (win_ms * 1e-3) / 1e9}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
