@@ -100,6 +100,7 @@ class PrefillInputs:
     cu_seqlens: np.ndarray     # [N+1] int32
     g_min: float = G_MIN
     dtype: str = "bf16"
+    gate: str = "bounded"      # "bounded" (g_min applies) or "softplus" (no lower bound)
 
     @property
     def T(self) -> int:
@@ -156,7 +157,8 @@ def cu_from_lengths(lens) -> np.ndarray:
 def make_prefill(seed: int, T: int, H: int, dtype: str = "bf16", *, A_std: float = 0.5,
                  lengths=None, varlen_total: Optional[int] = None, varlen_lo: int = 64,
                  varlen_hi: int = 16384, s0_std: float = 0.0, s0_docs: str = "first",
-                 z_mean: float = 0.0, z_std: float = 1.0, d: int = D) -> PrefillInputs:
+                 z_mean: float = 0.0, z_std: float = 1.0, d: int = D,
+                 gate: str = "bounded") -> PrefillInputs:
     """Generic prefill recipe.
 
     ``lengths`` gives explicit document lengths; ``varlen_total`` draws them
@@ -192,7 +194,7 @@ def make_prefill(seed: int, T: int, H: int, dtype: str = "bf16", *, A_std: float
             S0[1:] = rng.standard_normal((n_docs_for_s0 - 1, H, d, d), dtype=np.float32) \
                 * np.float32(s0_std)
     return PrefillInputs(q=q, k=k, v=v, z=z, beta=beta, A_log=A_log, S0=S0,
-                         cu_seqlens=cu_from_lengths(lens), dtype=dtype)
+                         cu_seqlens=cu_from_lengths(lens), dtype=dtype, gate=gate)
 
 
 # ----------------------------------------------------------------------------

@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 code with the GPU library (``linear_attention_fwd_amd``) and never imports it.
 
 Contents
-  * ``kda_oracle.c`` -- gate (eq. (5) of the "序列维度（下）" page) and the
+  * ``kda_oracle.c`` -- gate (eq. (5) of the "序列维度（下）" page, and the
+    unbounded Kimi Linear gate of the same section) and the
     token-by-token recurrence (eq. (1) of the systems page, delta form of the
     SemiAnalysis page), fp64, OpenMP over (document, head).
   * ``brute.py``     -- NumPy explicit-matrix form for tiny inputs
@@ -54,6 +55,9 @@ def _load():
     lib.kda_oracle_gate.argtypes = [dp, dp, ctypes.c_double, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, dp]
     lib.kda_oracle_gate.restype = None
+    lib.kda_oracle_gate_softplus.argtypes = [dp, dp, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, dp]
+    lib.kda_oracle_gate_softplus.restype = None
     lib.kda_oracle_recurrent.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, dp, dp,
                                          ctypes.c_int32]
@@ -83,6 +87,25 @@ def gate(z: np.ndarray, A_log: Optional[np.ndarray], g_min: float) -> np.ndarray
     g = np.empty_like(z)
     _load().kda_oracle_gate(_dptr(z), _dptr(A), float(g_min), T, H, dk, _dptr(g))
     return g
+
+
+def gate_softplus(z: np.ndarray, A_log: Optional[np.ndarray]) -> np.ndarray:
+    """Unbounded Kimi Linear gate g = -exp(A_h) * softplus(z) in fp64; z: [T, H, dk]."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    T, H, dk = z.shape
+    A = None if A_log is None else np.ascontiguousarray(A_log, dtype=np.float64)
+    g = np.empty_like(z)
+    _load().kda_oracle_gate_softplus(_dptr(z), _dptr(A), T, H, dk, _dptr(g))
+    return g
+
+
+def gate_of(inp, z: np.ndarray, heads=None) -> np.ndarray:
+    """The gate that ``inp`` names ("bounded": equation (5); "softplus": the
+    unbounded Kimi Linear map) on logits z [T, H', dk] of heads ``heads``."""
+    A = inp.A_log if heads is None else inp.A_log[heads]
+    if getattr(inp, "gate", "bounded") == "softplus":
+        return gate_softplus(z, A)
+    return gate(z, A, inp.g_min)
 
 
 def recurrent(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int = 0):
@@ -121,7 +144,7 @@ def recurrent(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int = 0):
 
 def forward(inp, nthreads: int = 0):
     """Full operator on a ``kda_gen.PrefillInputs``: gate, then the recurrence."""
-    g = gate(inp.z.f64(), inp.A_log, inp.g_min)
+    g = gate_of(inp, inp.z.f64())
     S0 = None if inp.S0 is None else inp.S0.astype(np.float64)
     return recurrent(inp.q.f64(), inp.k.f64(), inp.v.f64(), g, inp.beta.f64(), S0,
                      inp.cu_seqlens, nthreads)

@@ -12,6 +12,11 @@
  *          g = g_min * Sigmoid(exp(A_h) * z),   alpha = exp(g).
  *      A_h is one scalar per head; z and g are per key channel.
  *
+ *  kda_oracle_gate_softplus -- the unbounded gate that the same section gives
+ *      for Kimi Linear (as in GDN and Mamba-2), the map the bound replaces:
+ *          g = -exp(A_h) * Softplus(z),   Softplus(z) = log(1 + exp(z)),
+ *      so g ranges over (-inf, 0) with no lower bound.
+ *
  *  kda_oracle_recurrent -- the token recurrence of "Kimi K3 模型结构（7）：
  *      结构决定系统", section "KDA 上下文并行", equation (1):
  *          S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
@@ -47,6 +52,25 @@ void kda_oracle_gate(const double *z, const double *A_log, double g_min, int64_t
       for (int32_t c = 0; c < dk; ++c) {
         const double x = scale * zr[c];
         gr[c] = g_min * (1.0 / (1.0 + exp(-x)));
+      }
+    }
+  }
+}
+
+/* g[t,h,c] = -exp(A_log[h]) * softplus(z[t,h,c]); A_log may be NULL (= 0).
+ * softplus(x) is evaluated as max(x, 0) + log1p(exp(-|x|)), which equals
+ * log(1 + exp(x)) and never overflows. */
+void kda_oracle_gate_softplus(const double *z, const double *A_log, int64_t T, int32_t H,
+                              int32_t dk, double *g) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      const double scale = exp(A_log ? A_log[h] : 0.0);
+      const double *zr = z + (t * H + h) * (int64_t)dk;
+      double *gr = g + (t * H + h) * (int64_t)dk;
+      for (int32_t c = 0; c < dk; ++c) {
+        const double x = zr[c];
+        const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+        gr[c] = -scale * sp;
       }
     }
   }

@@ -62,10 +62,14 @@ MUTANTS = {
                                   "gr[c] = g_min * (1.0 / (1.0 + exp(x)));"),
     "gate_scale_outside_exp": _replace("const double scale = exp(A_log ? A_log[h] : 0.0);",
                                        "const double scale = 1.0 + (A_log ? A_log[h] : 0.0);"),
+    "softplus_wrong_branch": _replace("log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
+    "softplus_no_floor_term": _replace("(x > 0.0 ? x : 0.0) + log1p", "log1p"),
+    "softplus_sign": _replace("gr[c] = -scale * sp;", "gr[c] = scale * sp;"),
 }
 
 PIN_TESTS = [
     pins.test_gate_closed_forms,
+    pins.test_softplus_gate_closed_forms,
     pins.test_reduces_to_linear_attention,
     pins.test_delta_rule_retrieval,
     pins.test_decay_only_closed_form,

@@ -63,6 +63,34 @@ def test_gate_closed_forms(oracle_mod):
     assert np.allclose(oracle_mod.gate(zz, A, -2.0) * 2.5, lhs, rtol=0, atol=1e-14)
 
 
+def test_softplus_gate_closed_forms(oracle_mod):
+    """The unbounded Kimi Linear gate, g = -e^A softplus(z) ("序列维度（下）",
+    section "K3 的改动：下界衰减"): softplus(0) = ln 2, softplus(z) -> z for large
+    z (no floor), -> e^z for very negative z, softplus(z) - softplus(-z) = z, and
+    e^A multiplies outside."""
+    z = np.array([0.0, 40.0, -40.0, 1.0, -2.5, 700.0], dtype=np.float64).reshape(6, 1, 1)
+    g = oracle_mod.gate_softplus(z, np.zeros(1))[:, 0, 0]
+    assert abs(g[0] + math.log(2.0)) < 1e-15
+    assert abs(g[1] + 40.0) < 1e-12                 # linear, no lower bound
+    assert abs(g[2] + math.exp(-40.0)) < 1e-30       # tiny decay for very negative z
+    assert abs(g[3] + math.log(1.0 + math.e)) < 1e-15
+    assert abs(g[4] + math.log(1.0 + math.exp(-2.5))) < 1e-15
+    assert abs(g[5] + 700.0) < 1e-9                  # no overflow where exp(z) would
+    rng = _rng(1)
+    zz = rng.standard_normal((9, 3, 16)) * 4.0
+    gp = oracle_mod.gate_softplus(zz, None)
+    gm = oracle_mod.gate_softplus(-zz, None)
+    assert np.allclose(gm - gp, zz, rtol=0, atol=1e-12)  # sp(z) - sp(-z) = z
+    A = np.array([0.0, 0.9, -1.4])
+    assert np.allclose(oracle_mod.gate_softplus(zz, A), gp * np.exp(A)[None, :, None],
+                       rtol=1e-15, atol=0)
+    assert np.all(gp < 0)
+    # gate_of picks the map the inputs name
+    inp = kda_gen.make_prefill(3, 64, 2, "f32", gate="softplus")
+    assert np.array_equal(oracle_mod.gate_of(inp, inp.z.f64()),
+                          oracle_mod.gate_softplus(inp.z.f64(), inp.A_log))
+
+
 def test_gate_range_matches_page_numbers(oracle_mod):
     gold = json.load(open(GOLDEN))
     z = np.linspace(-30, 30, 2001).reshape(-1, 1, 1)
