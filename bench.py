@@ -76,10 +76,10 @@ def decode_state_bytes(N: int, H: int, D: int = 128) -> int:
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="prefill",
                     help="prefill: the single-sequence H=96 step (the reported metric); long: "
                          "the T=262144 H=8 segment scan; varlen: the packed 65536-token H=96 "
@@ -281,6 +281,21 @@ def main():
     ck_ms = float(np.mean([a.elapsed_time(c) for a, c in ck_ev]))
     ck_written = (T // interval - (1 if T % interval == 0 else 0)) * H * 128 * 128 * 4
 
+    # ---------------- the same step with the unbounded (softplus) gate ------
+    def unb_step():
+        kda.kda_chunk_fwd_unbounded(q, k, v, z, b, A_log, o=o, final_state=fin, workspace=ws)
+
+    for _ in range(args.warmup):
+        unb_step()
+    torch.cuda.synchronize()
+    unb_ev = _events(torch, stream, args.steps)
+    for i in range(args.steps):
+        unb_ev[i][0].record(stream)
+        unb_step()
+        unb_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    unb_ms = float(np.mean([a.elapsed_time(c) for a, c in unb_ev]))
+
     # ---------------- decode with speculative verify -------------------------
     # the decode workload (N=512, H=96, 4 drafts + bonus) plus, drawn after it, a
     # next window of 4 drafts for the fused replay + bonus + window step
@@ -380,6 +395,9 @@ def main():
                               "bytes": floor_bytes,
                               "GBps": floor_bytes / (step_kernel_ms * 1e-3) / 1e9,
                               "frac": floor_bytes / (step_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "unbounded_gate": {"gate": "-exp(A) softplus(z), diagonal subtiles per position in fp32",
+                           "kernels_ms": unb_ms, "extra_ms": unb_ms - step_kernel_ms,
+                           "tokens_per_s": T / (unb_ms * 1e-3)},
         "checkpoints": {"interval_tokens": interval, "kernels_ms": ck_ms,
                         "extra_ms": ck_ms - step_kernel_ms, "state_bytes_written": ck_written},
         "decode": {"workload": "N=512 H=96, 4 drafts + bonus, accepted U{0..4}, fp32 state",

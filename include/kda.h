@@ -165,6 +165,27 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
                               void *stream);
 
 /* ------------------------------------------------------------------------- */
+/* kda_chunk_fwd_unbounded -- kda_chunk_fwd with the unbounded gate.
+ *
+ * The same operator as kda_chunk_fwd with the per-step log-decay map that the
+ * bounded gate replaces ("Kimi K3 模型结构（2）：序列维度（下）", section
+ * "K3 的改动：下界衰减", the Kimi Linear form shared with GDN and Mamba-2):
+ *   g = -exp(A_h) * softplus(z),   softplus(z) = log(1 + exp(z)),
+ * which has no lower bound.  Without a bound the diagonal 16 x 16 subtiles of
+ * the intra-chunk matrices cannot be split into two factors for the matrix
+ * cores (same section): they are computed per position pair in fp32, the
+ * path whose cost the bounded gate removes; every other step is the one of
+ * kda_chunk_fwd.  Arguments as for kda_chunk_fwd without g_min and compute:
+ * bf16 inputs only (KDA_ERR_UNSUPPORTED otherwise), two-kernel path, a
+ * workspace of kda_chunk_fwd_workspace_size() bytes required. */
+int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const void *g_logits,
+                            const void *beta, const float *A_log, const float *initial_state,
+                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N,
+                            int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *o,
+                            float *final_state, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* ------------------------------------------------------------------------- */
 /* kda_segment_scan -- intra-device context parallelism for long prefill.
  *
  * Same operator and arguments as kda_chunk_fwd.  The packed sequence is cut into

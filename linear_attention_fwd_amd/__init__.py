@@ -7,6 +7,7 @@ tensors are not on a GPU, calls raise.
 
 Entry points (same names as the C ABI):
   * ``kda_chunk_fwd``    -- chunkwise prefill of packed documents
+  * ``kda_chunk_fwd_unbounded`` -- the same with the unbounded (softplus) gate
   * ``kda_segment_scan`` -- prefill with intra-device segment pairs + scan
   * ``kda_decode_step``  -- decode step with speculative-verify replay
   * ``kda_decode_step_window`` -- the same step fused with the next draft window
@@ -27,7 +28,8 @@ KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_prep",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_unbounded", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_prep",
            "kda_chunk_recurrence", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count",
            "kda_segment_scan",
            "kda_segment_scan_workspace_size",
@@ -60,6 +62,9 @@ def load_library(path: str = LIB_PATH):
     prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_unbounded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                            i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_fwd_unbounded.restype = ctypes.c_int
     lib.kda_chunk_fwd_checkpoints.argtypes = prefill[:-1] + [i32, vp, ctypes.c_size_t, vp, vp, vp,
                                                              ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_checkpoints.restype = ctypes.c_int
@@ -202,6 +207,33 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                            float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
                            dk, dv, _dtype_code(q), int(compute), _ptr(o), _ptr(final_state),
                            ws_ptr, ws_bytes, _stream())
+    _check(rc)
+    return o, final_state
+
+
+def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=None,
+                            cu_seqlens=None, cu_seqlens_host=None,
+                            output_final_state: bool = True, o=None, final_state=None,
+                            workspace=None) -> Tuple[object, Optional[object]]:
+    """``kda_chunk_fwd`` with the unbounded gate g = -exp(A_h) softplus(z) (bf16
+    inputs, two-kernel path).  Returns (o, final_state) as ``kda_chunk_fwd``."""
+    torch = _torch()
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
+                                                       initial_state, cu_seqlens, cu_seqlens_host)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, kda_chunk_fwd_workspace_size(N, T, H, dk, dv)),
+                                dtype=torch.uint8, device=q.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.kda_chunk_fwd_unbounded(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
+                                     _ptr(A_log), _ptr(initial_state), _ptr(cu_dev), host_ptr, N,
+                                     T, H, dk, dv, _dtype_code(q), _ptr(o), _ptr(final_state),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream())
     _check(rc)
     return o, final_state
 
@@ -407,5 +439,5 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
 
 __all__ = ["kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_decode_step_window",
-           "kda_chunk_fwd_checkpoints", "kda_checkpoint_count", "load_library", "KDAError",
+           "kda_chunk_fwd_unbounded", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count", "load_library", "KDAError",
            "KDA_COMPUTE_AUTO", "KDA_COMPUTE_F32"]

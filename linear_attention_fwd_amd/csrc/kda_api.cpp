@@ -276,6 +276,36 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
   return KDA_OK;
 }
 
+int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const void *g_logits,
+                            const void *beta, const float *A_log, const float *initial_state,
+                            const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N,
+                            int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *o,
+                            float *final_state, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  const float unused_g_min = -5.0f;  // the unbounded gate takes no g_min
+  int rc = check_prefill(q, k, v, g_logits, beta, unused_g_min, cu_seqlens, cu_seqlens_host, N, T,
+                         H, dk, dv, dtype, KDA_COMPUTE_AUTO, o);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_BF16)
+    return fail(KDA_ERR_UNSUPPORTED, "the unbounded gate runs on the bf16 two-kernel path only");
+  rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+  if (rc != KDA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, unused_g_min, initial_state,
+                                      cu_seqlens, N, T, H, o, final_state, workspace);
+    p.gate = kda::GATE_SOFTPLUS;
+    hipError_t e = kda::launch_chunk_prep(p, st);
+    if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded empty documents");
+  }
+  return KDA_OK;
+}
+
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv) {
   if (N <= 0 || T < 0 || H <= 0 || dk != kD || dv != kD) return 0;
   return kda::split_workspace_bytes(T, N, H);

@@ -203,6 +203,7 @@ __device__ __forceinline__ int doc_of_slot(const int32_t *cu, int N, int64_t slo
 struct PrepLds {
   float GC2[D];       // G_C (base 2)
   float Gref[4][D];   // G (base 2) at the first token of each subtile
+  float Gend[4][D];   // G (base 2) at the last token of each subtile (unbounded gate)
   float F[6][D];      // e^(Gref[I] - Gref[J]) for I > J
   float beta[CH];
   float wtot[4][D];   // per-wave cumulative-sum totals
@@ -210,19 +211,23 @@ struct PrepLds {
 
 // a1: gate and inclusive cumulative sum over the chunk (base 2).  Tokens at or
 // beyond len are padding: no decay.  Leaves G[r][c] for this thread's tokens
-// and channels, beta, Gref and GC2 in LDS; ends with a barrier.
-template <class IO>
+// and channels, beta, Gref and GC2 in LDS (and Gend for the unbounded gate);
+// ends with a barrier.  UNB selects the unbounded gate (gmin2 unused).
+template <class IO, bool UNB = false>
 __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO::raw8 (&Rz)[4],
                                                  typename IO::raw1 Rb, float c1, float gmin2,
                                                  int len, int tid, int w, int tq, int cg,
                                                  float (&G)[4][8]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float gm = (16 * w + 4 * tq + r < len) ? gmin2 : 0.f;
+    const bool tok = 16 * w + 4 * tq + r < len;
+    const float gm = tok ? gmin2 : 0.f;
+    const float cm = tok ? c1 : 0.f;
     float zz[8];
     IO::cvt8(Rz[r], zz);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) G[r][c] = kda_gate2(zz[c], c1, gm);
+    for (int c = 0; c < 8; ++c)
+      G[r][c] = UNB ? kda_gate2_softplus(zz[c], cm) : kda_gate2(zz[c], c1, gm);
   }
   if (tid < CH) ps.beta[tid] = IO::cvt1(Rb);
   // in-lane over r, across the 4 token groups of the wave (lanes 16 apart),
@@ -271,6 +276,10 @@ __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO:
     *reinterpret_cast<float4 *>(&ps.GC2[8 * cg]) = make_float4(G[3][0], G[3][1], G[3][2], G[3][3]);
     *reinterpret_cast<float4 *>(&ps.GC2[8 * cg + 4]) = make_float4(G[3][4], G[3][5], G[3][6], G[3][7]);
   }
+  if (UNB && tq == 3) {
+    *reinterpret_cast<float4 *>(&ps.Gend[w][8 * cg]) = make_float4(G[3][0], G[3][1], G[3][2], G[3][3]);
+    *reinterpret_cast<float4 *>(&ps.Gend[w][8 * cg + 4]) = make_float4(G[3][4], G[3][5], G[3][6], G[3][7]);
+  }
   __syncthreads();
   SCHED_FENCE();
 }
@@ -280,7 +289,18 @@ __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO:
 // kh_sink(r, i, kh[8]) (token 16w + 4tq + r = i); per token row i the sink
 // receives K_decay and Q_decay (row_sink(i, kdec[8], qdec[8])); K_restore is
 // returned for the caller to store.
-template <class Ar, class IO, class KhSink, class RowSink>
+//
+// The query side (Qh, Kh) is referenced to the first token s of the subtile,
+// e^(G_i - G_s) <= 1.  For the bounded gate the key side Ki is referenced to
+// that token too, e^(G_s - G_j) < e^75 (g >= -5 per step over at most 15
+// steps), so even the diagonal subtile products split into two factors
+// ("序列维度（下）", section on the 16-token subtiles).  Without a lower bound
+// (UNB) that factor has no bound, so the key side is referenced to the last
+// token e of its subtile instead, e^(G_e - G_j) <= 1: off-diagonal pairs then
+// take the factor e^(G_s(I) - G_e(J)) <= 1 and the diagonal subtiles are done
+// per position (prep_diag_positions).  K_restore = e^(G_C - G_j) k_j is Ki
+// times e^(G_C - G_ref), in the unbounded case a product of factors <= 1.
+template <class Ar, class IO, bool UNB = false, class KhSink, class RowSink>
 __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename Ar::E *Qh,
                                                     KhSink &&kh_sink, typename Ar::E *Ki,
                                                     const typename IO::raw8 (&Rq)[4],
@@ -288,12 +308,13 @@ __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename 
                                                     const float (&G)[4][8], int w, int tq, int cg,
                                                     float (&Kres)[4][8], RowSink &&row_sink) {
   using TD = Tile<typename Ar::E, D>;
-  float Pj[8], Rj[8], gref[8];
+  float Pj[8], Rj[8], gref[8], gkey[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     gref[c] = ps.Gref[w][8 * cg + c];
+    gkey[c] = UNB ? ps.Gend[w][8 * cg + c] : gref[c];
     Pj[c] = __builtin_amdgcn_exp2f(gref[c]);                       // e^(G_s)
-    Rj[c] = __builtin_amdgcn_exp2f(ps.GC2[8 * cg + c] - gref[c]);  // e^(G_C - G_s) <= 1
+    Rj[c] = __builtin_amdgcn_exp2f(ps.GC2[8 * cg + c] - gkey[c]);  // e^(G_C - G_ref) <= 1
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -304,7 +325,8 @@ __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename 
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float e1 = __builtin_amdgcn_exp2f(G[r][c] - gref[c]);  // <= 1
-      const float e2 = __builtin_amdgcn_rcpf(e1);                   // < e^75
+      // bounded: 1 / e1 < e^75; unbounded: e^(G_e - G_i) <= 1
+      const float e2 = UNB ? __builtin_amdgcn_exp2f(gkey[c] - G[r][c]) : __builtin_amdgcn_rcpf(e1);
       qh[c] = qv[c] * e1;
       kh[c] = kv[c] * e1;
       ki[c] = kv[c] * e2;
@@ -322,13 +344,16 @@ __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename 
   }
 }
 
-// F[pair][c] = e^(Gref[I][c] - Gref[J][c]), pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+// F[pair][c] = e^(Gref[I][c] - Gref[J][c]) (UNB: e^(Gref[I][c] - Gend[J][c]) <= 1),
+// pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2): moves the key side's reference to
+// the first token of the query subtile
+template <bool UNB = false>
 __device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
   for (int x = tid; x < 6 * D; x += FWD_THREADS) {
     const int pi = x / D, c = x % D;
     const int I = (pi == 0) ? 1 : (pi < 3 ? 2 : 3);
     const int J = (pi == 0) ? 0 : (pi < 3 ? pi - 1 : pi - 3);
-    ps.F[pi][c] = __builtin_amdgcn_exp2f(ps.Gref[I][c] - ps.Gref[J][c]);
+    ps.F[pi][c] = __builtin_amdgcn_exp2f(ps.Gref[I][c] - (UNB ? ps.Gend[J][c] : ps.Gref[J][c]));
   }
 }
 
@@ -337,9 +362,10 @@ __device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
 // with row j of the pair's tile at columns 4g..4g+3 and writes them at once.
 // L (natural order, operand precision) goes to LDS; M_qk goes to
 // mqk_sink(row, J, mq[4]).  PRODUCTS selects M_qk (1), L (2) or both (3); a
-// product not selected reads nothing from its tile (Qh or Kh).
+// product not selected reads nothing from its tile (Qh or Kh).  SKIP_DIAG
+// leaves the diagonal pairs (I = J) to prep_diag_positions.
 constexpr int PROD_MQK = 1, PROD_L = 2;
-template <class Ar, int PRODUCTS, class MqkSink>
+template <class Ar, int PRODUCTS, bool SKIP_DIAG = false, class MqkSink>
 __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const typename Ar::E *Qh,
                                                       const typename Ar::E *Kh,
                                                       const typename Ar::E *Ki, typename Ar::E *L,
@@ -349,6 +375,7 @@ __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const t
   for (int pidx = w; pidx < 10; pidx += 4) {
     const int I = (pidx == 0) ? 0 : (pidx < 3 ? 1 : (pidx < 6 ? 2 : 3));
     const int J = pidx - I * (I + 1) / 2;
+    if (SKIP_DIAG && I == J) continue;
     floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -374,6 +401,110 @@ __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const t
     }
     if constexpr ((PRODUCTS & PROD_MQK) != 0) mqk_sink(row, J, mq);
     if constexpr ((PRODUCTS & PROD_L) != 0) Ar::store4(&L[TL::idx(row, 16 * J + 4 * g)], lk);
+  }
+}
+
+// Sum of v[0..15] over the 16 lanes of a row group (lanes 16tq + cg), split so
+// that lane cg keeps element cg: four halving steps, each lane keeping the
+// half its lane bit selects and adding its partner's copy of that half.
+__device__ __forceinline__ float reduce_scatter16(const float (&v)[16], int cg) {
+  float a[8], b[4], c[2];
+  const bool h8 = cg & 8, h4 = cg & 4, h2 = cg & 2, h1 = cg & 1;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+    a[x] = (h8 ? v[8 + x] : v[x]) + __shfl_xor(h8 ? v[x] : v[8 + x], 8);
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    b[x] = (h4 ? a[4 + x] : a[x]) + __shfl_xor(h4 ? a[x] : a[4 + x], 4);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    c[x] = (h2 ? b[2 + x] : b[x]) + __shfl_xor(h2 ? b[x] : b[2 + x], 2);
+  return (h1 ? c[1] : c[0]) + __shfl_xor(h1 ? c[0] : c[1], 1);
+}
+
+// LDS writes of this wave become visible to its other lanes (wave-local data)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// a3 on the diagonal subtiles when the gate has no lower bound: subtile I = w
+// (this wave's own 16 tokens) from the definition, one position pair at a time
+// in fp32, the path that the bound removes ("序列维度（下）", section on the
+// 16-token subtiles): for j <= i in the subtile
+//   M_qk[i][j] = sum_c q_ic k_jc e^(G_ic - G_jc),
+//   L[i][j]    = beta_i sum_c k_ic k_jc e^(G_ic - G_jc)   (j < i only),
+// where e^(G_ic - G_jc) <= 1 never overflows.  The wave stages its tokens'
+// q, k (bf16, as read) and G (fp32) in `stage` (8 KB of LDS of its own), 64
+// channels at a time.  Lane (tq, cg) takes subtile rows tq, 7 - tq, 8 + tq and
+// 15 - tq (34 position pairs for every lane) and channels 4cg..4cg+3 of each
+// half; the channel sums are then spread over the 16 lanes of the row group,
+// lane cg keeping column cg.  M_qk goes to mqk_sink(row, col, value) (zeros
+// above the diagonal included), L to the L tile.
+template <class MqkSink>
+__device__ __forceinline__ void prep_diag_positions(char *stage,
+                                                    const bufio<bf16_t>::raw8 (&Rq)[4],
+                                                    const bufio<bf16_t>::raw8 (&Rk)[4],
+                                                    const float (&G)[4][8], const float *beta,
+                                                    bf16_t *L, int w, int tq, int cg,
+                                                    MqkSink &&mqk_sink) {
+  using TL = Tile<bf16_t, CH>;
+  constexpr int HC = 64;  // channels staged at a time
+  float *Gs = reinterpret_cast<float *>(stage);              // [16][HC]
+  bf16_t *Qs = reinterpret_cast<bf16_t *>(stage + 16 * HC * 4);  // [16][HC]
+  bf16_t *Ks = Qs + 16 * HC;                                     // [16][HC]
+  const int c0 = 4 * cg;
+#pragma unroll 1
+  for (int s = 0; s < 4; ++s) {
+    const int row = (s == 0) ? tq : (s == 1) ? 7 - tq : (s == 2) ? 8 + tq : 15 - tq;
+    constexpr int NJ_MAX = 16;
+    const int nj = 4 * (s + 1);  // rows of slot s are at most 4s + 3
+    float m[NJ_MAX], l[NJ_MAX];
+#pragma unroll
+    for (int jj = 0; jj < NJ_MAX; ++jj) m[jj] = l[jj] = 0.f;
+#pragma unroll 1
+    for (int hf = 0; hf < 2; ++hf) {
+      wave_lds_sync();  // earlier reads of the staging area are done
+      if ((cg >> 3) == hf) {
+        const int lc = 8 * (cg & 7);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * tq + r;
+          *reinterpret_cast<float4 *>(&Gs[i * HC + lc]) = make_float4(G[r][0], G[r][1], G[r][2], G[r][3]);
+          *reinterpret_cast<float4 *>(&Gs[i * HC + lc + 4]) = make_float4(G[r][4], G[r][5], G[r][6], G[r][7]);
+          *reinterpret_cast<u32x4 *>(&Qs[i * HC + lc]) = Rq[r].a;
+          *reinterpret_cast<u32x4 *>(&Ks[i * HC + lc]) = Rk[r].a;
+        }
+      }
+      wave_lds_sync();
+      const float4 gi = *reinterpret_cast<const float4 *>(&Gs[row * HC + c0]);
+      const floatx4 qi = Arith<false>::load4(&Qs[row * HC + c0]);
+      const floatx4 ki = Arith<false>::load4(&Ks[row * HC + c0]);
+      const float giv[4] = {gi.x, gi.y, gi.z, gi.w};
+#pragma unroll
+      for (int jj = 0; jj < NJ_MAX; ++jj) {
+        if (jj < nj) {
+          const float4 gj = *reinterpret_cast<const float4 *>(&Gs[jj * HC + c0]);
+          const floatx4 kj = Arith<false>::load4(&Ks[jj * HC + c0]);
+          const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+          const bool lower = jj <= row;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // e^(G_i - G_j) in base 2; -inf (factor 0) above the diagonal
+            const float x = lower ? giv[c] - gjv[c] : -__builtin_inff();
+            const float t = kj[c] * __builtin_amdgcn_exp2f(x);
+            m[jj] = fmaf(qi[c], t, m[jj]);
+            l[jj] = fmaf(ki[c], t, l[jj]);
+          }
+        }
+      }
+    }
+    const float mv = reduce_scatter16(m, cg);
+    const float lv = reduce_scatter16(l, cg);
+    const int i = 16 * w + row;
+    mqk_sink(i, 16 * w + cg, mv);
+    L[TL::idx(i, 16 * w + cg)] = f32_to_bf16(cg < row ? beta[i] * lv : 0.f);
   }
 }
 

@@ -303,6 +303,15 @@ template <typename E, int COLS> struct Tile {
 __device__ __forceinline__ float kda_gate2(float z, float c1, float gm) {
   return gm * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(c1 * z));
 }
+// Unbounded gate that the same section gives for Kimi Linear (as in GDN and
+// Mamba-2), g = -exp(A_h) softplus(z), in base-2 units: c1 = -exp(A_h) log2 e,
+// or 0 for a padding row.  softplus(z) = max(z, 0) + ln(1 + e^-|z|), which
+// cannot overflow.
+__device__ __forceinline__ float kda_gate2_softplus(float z, float c1) {
+  const float t = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(z));  // e^-|z|
+  const float sp = fmaxf(z, 0.0f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + t);
+  return c1 * sp;
+}
 // The same gate in natural-log units (decode path).
 __device__ __forceinline__ float kda_gate(float z, float escale, float g_min) {
   const float x = escale * z;

@@ -68,7 +68,11 @@ struct SplitParams {
   // (not after its last chunk) to ckpt[slot / ckpt_chunks, H, D, D]; 0 = none
   float *ckpt;
   int ckpt_chunks;
+  // gate map: GATE_BOUNDED (g_min * sigmoid) or GATE_SOFTPLUS (unbounded,
+  // g_min unused); only the prep kernel depends on it
+  int gate;
 };
+constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
 size_t split_workspace_bytes(int64_t T, int N, int H);
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);

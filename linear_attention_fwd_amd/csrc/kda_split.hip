@@ -86,6 +86,10 @@ struct __align__(16) PrepSmem {
 };
 static_assert(3 * sizeof(PrepSmem) <= 160 * 1024, "three prep workgroups per compute unit");
 
+// UNB: the unbounded Kimi Linear gate; the diagonal subtiles of M_qk and L are
+// then formed per position (prep_diag_positions) and the off-diagonal ones
+// with the key side referenced to the end of its subtile.
+template <bool UNB>
 __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitParams p) {
   using Ar = Arith<false>;
   using IO = bufio<bf16_t>;
@@ -142,13 +146,23 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
   }
 
   float G[4][8];
-  prep_gate_cumsum<IO>(sm.ps, Rz, Rb, c1, gmin2, len, tid, w, tq, cg, G);  // two barriers
+  prep_gate_cumsum<IO, UNB>(sm.ps, Rz, Rb, c1, gmin2, len, tid, w, tq, cg, G);  // two barriers
 
   const __amdgpu_buffer_rsrc_t ri =
       make_rsrc((char *)p.ws + ((int64_t)h * p.n_slots + slot) * IMG_BYTES, IMG_BYTES);
+  if constexpr (UNB) {
+    static_assert(sizeof(sm.u) >= 4 * 8192, "per-wave staging for the diagonal subtiles");
+    prep_diag_positions(reinterpret_cast<char *>(&sm.u) + w * 8192, Rq, Rk, G, sm.ps.beta, sm.L,
+                        w, tq, cg, [&](int row, int col, float m) {
+                          __builtin_amdgcn_raw_buffer_store_b16(
+                              f32_to_bf16(m), ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(col)), 0, 0);
+                        });
+    __syncthreads();  // the staging area becomes the subtile operand tiles
+    SCHED_FENCE();
+  }
   float Kres[4][8];
   bf16x4 kh_keep[4][2];  // key-side subtile operand of this thread's 4 tokens x 8 channels
-  prep_decay_operands<Ar, IO>(sm.ps, sm.u.p1.QKh,
+  prep_decay_operands<Ar, IO, UNB>(sm.ps, sm.u.p1.QKh,
                               [&](int r, int, const float *kh) {
                                 kh_keep[r][0] = to_bf16x4(floatx4{kh[0], kh[1], kh[2], kh[3]});
                                 kh_keep[r][1] = to_bf16x4(floatx4{kh[4], kh[5], kh[6], kh[7]});
@@ -167,12 +181,12 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
     const float x[4] = {Kres[0][c], Kres[1][c], Kres[2][c], Kres[3][c]};
     img_st4(ri, OFF_KRT + 2 * TC::idx(8 * cg + c, kperm(16 * w + 4 * tq)), x);
   }
-  prep_pair_factors(sm.ps, tid);
+  prep_pair_factors<UNB>(sm.ps, tid);
   if (tid < D) buf_st_f32(ri, __builtin_amdgcn_exp2f(sm.ps.GC2[tid]), OFF_GAMC + 4 * tid);
   __syncthreads();
   SCHED_FENCE();
 
-  prep_subtile_products<Ar, PROD_MQK>(sm.ps, sm.u.p1.QKh, nullptr, sm.u.p1.Ki, sm.L, w, g, j,
+  prep_subtile_products<Ar, PROD_MQK, UNB>(sm.ps, sm.u.p1.QKh, nullptr, sm.u.p1.Ki, sm.L, w, g, j,
                                       [&](int row, int J, const float *mq) {
                                         img_st4(ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(16 * J + 4 * g)), mq);
                                       });
@@ -186,7 +200,7 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
   }
   __syncthreads();
   SCHED_FENCE();
-  prep_subtile_products<Ar, PROD_L>(sm.ps, nullptr, sm.u.p1.QKh, sm.u.p1.Ki, sm.L, w, g, j,
+  prep_subtile_products<Ar, PROD_L, UNB>(sm.ps, nullptr, sm.u.p1.QKh, sm.u.p1.Ki, sm.L, w, g, j,
                                     [](int, int, const float *) {});
   // The recurrence reads the upper blocks (0,1) and (2,3) of M_qk and INV Diag(beta)
   // (its 32-wide k steps span two subtiles); they must hold zeros.
@@ -657,7 +671,12 @@ size_t split_workspace_bytes(int64_t T, int N, int H) {
 
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
   const int64_t blocks = p.n_slots * p.H;
-  hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3((unsigned)blocks), dim3(FWD_THREADS), 0, stream, p);
+  if (p.gate == GATE_SOFTPLUS)
+    hipLaunchKernelGGL(kda_chunk_prep_kernel<true>, dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(kda_chunk_prep_kernel<false>, dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

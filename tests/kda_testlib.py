@@ -59,7 +59,7 @@ def oracle_forward(inp, heads=None, group=8):
     S = np.zeros((inp.N, len(heads), 128, 128))
     for g0 in range(0, len(heads), group):
         hs = heads[g0:g0 + group]
-        gg = oracle.gate(_slice_f32(inp.z, hs).astype(np.float64), inp.A_log[hs], inp.g_min)
+        gg = oracle.gate_of(inp, _slice_f32(inp.z, hs).astype(np.float64), hs)
         S0 = None if inp.S0 is None else inp.S0[:, hs].astype(np.float64)
         oo, SS = oracle.recurrent(_slice_f32(inp.q, hs), _slice_f32(inp.k, hs),
                                   _slice_f32(inp.v, hs), gg, _slice_f32(inp.beta, hs), S0,
@@ -88,6 +88,17 @@ def gpu_chunk_fwd(inp, compute=0, t=None, fused=False):
     o, S = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min,
                              t["S0"], t["cu"], t["cu_host"], compute=compute,
                              workspace=False if fused else None)
+    torch.cuda.synchronize()
+    return kda_gen.from_torch(o), kda_gen.from_torch(S)
+
+
+def gpu_chunk_fwd_unbounded(inp, t=None):
+    """kda_chunk_fwd_unbounded (softplus gate) on the GPU."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    t = t or gpu_inputs(inp)
+    o, S = kda.kda_chunk_fwd_unbounded(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
+                                       t["S0"], t["cu"], t["cu_host"])
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 

@@ -218,6 +218,21 @@ def test_decode_validation(lib):
     assert lib.kda_last_error() is not None
 
 
+def test_unbounded_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, T=256, H=4, dtype=1, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        q = a["q"]
+        return lib.kda_chunk_fwd_unbounded(q, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 1,
+                                           a["T"], a["H"], 128, 128, a["dtype"], FAKE, None,
+                                           a["ws"], a["ws_bytes"], None)
+    assert call(q=None) == KDA_ERR_NULL
+    assert call(dtype=0) == KDA_ERR_UNSUPPORTED     # fp32 inputs: bf16 path only
+    assert call(ws=None) == KDA_ERR_WORKSPACE
+    assert call(ws_bytes=100) == KDA_ERR_WORKSPACE
+    assert call(H=0) == KDA_ERR_SHAPE
+
+
 def test_decode_window_validation(lib):
     def call(**kw):
         a = dict(state=FAKE, c=FAKE, acc=FAKE, W=4, n=FAKE, w=FAKE, W2=4, o=FAKE, ow=FAKE,

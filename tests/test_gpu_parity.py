@@ -11,7 +11,7 @@ import pytest
 
 import kda_gen
 from kda_testlib import (TOL_BF16, TOL_BF16_STORAGE, TOL_F32, gpu_chunk_fwd, gpu_decode,
-                         gpu_decode_window, gpu_segment_scan,
+                         gpu_decode_window, gpu_segment_scan, gpu_chunk_fwd_unbounded,
                          decode_gpu_inputs, oracle_forward, rel_l2_slices)
 import oracle
 
@@ -275,6 +275,38 @@ def test_segment_scan_one_segment_equals_chunk_fwd():
     o1, S1 = gpu_chunk_fwd(inp, compute=1)
     o2, S2 = gpu_segment_scan(inp, n_segments=1, compute=1)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+# ---------------------------------------------------------------------------
+# the unbounded (softplus) gate: per-position diagonal subtiles
+# ---------------------------------------------------------------------------
+UNBOUNDED_CASES = {
+    # ordinary logits: decays of the same order as the bounded gate's
+    "single_ragged_1000": dict(seed=61, T=1000, H=4),
+    # strong decays (per-step log-decay down to about -100): a 16-token subtile
+    # spans far more than the fp32 exponent range, so only the per-position path
+    # can form its diagonal block; documents with initial states, a ragged tail
+    "strong_decay_varlen": dict(seed=62, T=1500, H=4, lengths=[700, 13, 64, 723], z_mean=2.0,
+                                z_std=3.0, A_std=1.0, s0_std=0.05, s0_docs="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNBOUNDED_CASES))
+def test_unbounded_gate_matches_oracle(name):
+    c = dict(UNBOUNDED_CASES[name])
+    seed, T, H = c.pop("seed"), c.pop("T"), c.pop("H")
+    inp = kda_gen.make_prefill(seed, T, H, "bf16", gate="softplus", **c)
+    print(f"[case] unbounded gate {name} T={T} H={H} N={inp.N}", flush=True)
+    if name == "strong_decay_varlen":
+        G = np.cumsum(oracle.gate_softplus(inp.z.f64()[:16], inp.A_log), axis=0)
+        assert (G[0] - G[15]).max() > 100.0  # e^100 is beyond fp32
+    o_ref, S_ref = oracle_forward(inp)
+    o, S = gpu_chunk_fwd_unbounded(inp)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    eo, _ = rel_l2_slices(o, o_ref, inp.cu_seqlens)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    print(f"    o: {eo:.3e}  state: {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
 # ---------------------------------------------------------------------------
