@@ -11,7 +11,8 @@ import pytest
 import kda_gen
 import oracle
 from kda_testlib import (TOL_BF16, TOL_BF16_STORAGE, TOL_F32, gpu_chunk_fwd, gpu_decode,
-                         gpu_inputs, gpu_segment_scan, oracle_forward, rel_l2_slices)
+                         gpu_decode_window, gpu_inputs, gpu_segment_scan, oracle_forward,
+                         rel_l2_slices)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,3 +88,78 @@ def test_decode_workload():
     es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
     print(f"[decode] o max {eo:.3e} | state max {es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_F32
+
+
+# ---------------------------------------------------------------------------
+# the next items at the sizes bench.py times them
+# ---------------------------------------------------------------------------
+def test_single_sequence_checkpoints_workload():
+    """Checkpoints every 512 tokens of the single-sequence workload (15 of them)
+    against the oracle on sampled heads: the oracle runs the sequence piece by
+    piece, each piece from the state the previous one ends with, and the state
+    after each piece is the checkpoint.  O and the final state are those of
+    kda_chunk_fwd, bit for bit."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    inp = kda_gen.workload(1)
+    interval = 512
+    print(f"[case] checkpoints every {interval} tokens, T=8192 H=96", flush=True)
+    t = gpu_inputs(inp)
+    o1, S1 = gpu_chunk_fwd(inp, t=t)
+    o2, S2, ck = kda.kda_chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["z"], t["beta"],
+                                               interval, t["A_log"], inp.g_min)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, kda_gen.from_torch(o2)) and np.array_equal(S1, kda_gen.from_torch(S2))
+    ck = kda_gen.from_torch(ck)
+    assert ck.shape[0] == kda.kda_checkpoint_count(1, inp.T, interval)
+    assert all(kda.checkpoint_index(None, 0, j, interval) == j - 1 < ck.shape[0] for j in range(1, 16))
+    heads = list(range(0, 96, 12))
+    q, k, v, b = (x.f64()[:, heads] for x in (inp.q, inp.k, inp.v, inp.beta))
+    g = oracle.gate(inp.z.f64()[:, heads], inp.A_log[heads], inp.g_min)
+    S = None
+    worst = 0.0
+    for j in range(1, inp.T // interval):
+        a, e = (j - 1) * interval, j * interval
+        _, S = oracle.recurrent(q[a:e], k[a:e], v[a:e], g[a:e], b[a:e], S)
+        assert np.all(np.isfinite(ck[j - 1]))
+        err, _ = rel_l2_slices(ck[j - 1][None, heads], S, axis_tokens=False)
+        worst = max(worst, err)
+    print(f"    15 checkpoints x {len(heads)} heads, max rel L2 {worst:.3e}", flush=True)
+    assert worst <= TOL_BF16
+
+
+def test_unbounded_gate_single_sequence_workload():
+    """The single-sequence workload with the unbounded softplus gate in place of the
+    bounded one (same logits), against the oracle on sampled heads."""
+    import dataclasses
+    import linear_attention_fwd_amd as kda
+    import torch
+    inp = dataclasses.replace(kda_gen.workload(1), gate="softplus")
+    print("[case] unbounded gate, T=8192 H=96", flush=True)
+    t = gpu_inputs(inp)
+    o, S = kda.kda_chunk_fwd_unbounded(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"])
+    torch.cuda.synchronize()
+    o, S = kda_gen.from_torch(o), kda_gen.from_torch(S)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    heads = list(range(0, 96, 6))
+    o_ref, S_ref = oracle_forward(inp, heads=heads, group=16)
+    eo, es = _report("unbounded gate, 16 sampled heads", o[:, heads], o_ref, S[:, heads], S_ref,
+                     inp.cu_seqlens)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_decode_window_workload():
+    """The decode workload with a next window of 4 drafts (the configuration
+    bench.py times): bonus output and state bit for bit those of kda_decode_step,
+    the window's outputs against the oracle."""
+    inp = kda_gen.make_decode(4, 512, 96, 4, "bf16", W2=4)
+    print("[case] decode N=512 H=96 W=4 + next window of 4", flush=True)
+    o_ref, ow_ref, S_ref = oracle.decode_window(inp)
+    o, ow, S = gpu_decode_window(inp)
+    o1, S1 = gpu_decode(inp)
+    assert np.array_equal(o, o1) and np.array_equal(S, S1)
+    ew = max(rel_l2_slices(ow[:, j][:, :, None], ow_ref[:, j][:, :, None], axis_tokens=False)[0]
+             for j in range(4))
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    print(f"[decode window] window o max {ew:.3e} | state max {es:.3e}", flush=True)
+    assert ew <= TOL_BF16 and es <= TOL_F32
