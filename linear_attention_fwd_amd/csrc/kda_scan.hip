@@ -358,14 +358,17 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
   if (sc.mode == 1) write_state(sc.composed + ((int64_t)chain * sc.H + h) * (D * 2 * D), 2 * D, X);
 }
 
-// The widest slice that still gives every compute unit a workgroup: each step
-// then streams M once for more columns.  (128-column slices of 8 waves timed
-// no faster.)  Chains too few for that (the scan of
-// the group pairs) take 16 columns per workgroup, where the step latency of
-// few workgroups decides.
+// A step is bound by the latency of its dependent loads and products, which
+// more workgroups per compute unit hide: about four do best (the compose of
+// 128 chains x 256 columns: 64-column slices, two per CU, 2.19 ms for the
+// whole long-prefill step; 32-column slices, four per CU, 2.17 ms; 16-column
+// slices, eight per CU, 2.26 ms).  So 64-column slices are taken only where
+// they already give four per CU, 32-column slices where they give two, and
+// chains too few for that (the scan of the group pairs) take 16 columns per
+// workgroup.  (128-column slices of 8 waves timed no faster.)
 hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream) {
   const int64_t units = (int64_t)sc.n_chains * sc.H;
-  if (units * (sc.ncols / 64) >= (int64_t)n_cu) {
+  if (units * (sc.ncols / 64) >= 4 * (int64_t)n_cu) {
     hipLaunchKernelGGL((kda_scan_chains_kernel<4, 1>), dim3(scan_grid(units, sc.ncols / 64)), dim3(512),
                        0, stream, sc);
   } else if (units * (sc.ncols / 32) >= 2 * (int64_t)n_cu) {

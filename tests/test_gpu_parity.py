@@ -169,6 +169,22 @@ def test_segment_scan_many_segments_wide_recurrence():
     _check_prefill(inp, o, S, _tols(inp, 0))
 
 
+def test_segment_scan_wide_compose():
+    """A compose of 8 groups x 32 heads = 256 chains over 256 columns: enough for
+    64-column slices at four per compute unit (the widest shape of the chain
+    kernel); 64 segments of one chunk slot, a ragged last document."""
+    import linear_attention_fwd_amd as kda
+    inp = kda_gen.make_prefill(50, 4096 - 37, 32, "bf16", lengths=[1500, 2559], s0_std=0.05,
+                               s0_docs="all")
+    _case(inp, 0)
+    n_cu = kda.kda_default_segments()
+    print(f"    n_segments=64 ({n_cu} compute units)", flush=True)
+    if 8 * inp.H * 4 < 4 * n_cu:
+        pytest.skip("this device needs more chains for the widest compose shape")
+    o, S = gpu_segment_scan(inp, n_segments=64)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+
+
 CHECKPOINT_CASES = {
     # name: (generator kwargs, interval in tokens)
     "varlen_128": (dict(seed=47, T=2300, H=3, dtype="bf16", lengths=[700, 0, 129, 1024, 383, 64],
