@@ -75,13 +75,19 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
   // Stream the state slice into registers: 16 rows x 4 columns per lane.  The
   // state is touched once per step, so its loads and stores are non-temporal
   // (measured on a plain in-place stream of this size: 5.2 TB/s with ordinary
-  // accesses, 5.4 TB/s with non-temporal ones).
+  // accesses, 5.4 TB/s with non-temporal ones).  Each wave keeps at most three
+  // of its 16 loads (and later of its 16 stores) in flight: left to the
+  // compiler, every wave issues all 16 at once, and the whole step ran at 5.33
+  // TB/s of state traffic; with the loads and stores metered in pairs it runs
+  // at 6.06 TB/s (at most one or two in flight: 5.98-6.01; at most eight:
+  // 5.55; one at a time: 4.34).
   float s[16][4];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const floatx4 x =
         __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(Sg + (row0 + i) * D + col0));
     s[i][0] = x[0]; s[i][1] = x[1]; s[i][2] = x[2]; s[i][3] = x[3];
+    if ((i & 1) && i != 15) wait_vmem_except_last<1>();
   }
 
   const float escale = __expf(A_log ? A_log[h] : 0.0f);
@@ -180,9 +186,13 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
       }
       if (t == acc) {  // the state after the bonus token is the one kept
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 16; ++i) {
           __builtin_nontemporal_store(floatx4{s[i][0], s[i][1], s[i][2], s[i][3]},
                                       reinterpret_cast<floatx4 *>(Sg + (row0 + i) * D + col0));
+          // metered as the loads, unless the next window's drafts follow: their
+          // work would then wait behind the stores instead of overlapping them
+          if ((i & 1) && i != 15 && win.W2 == 0) wait_vmem_except_last<1>();
+        }
       }
     }
     __syncthreads();  // the staging buffers are rewritten by the next batch
