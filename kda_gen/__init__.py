@@ -101,6 +101,7 @@ class PrefillInputs:
     g_min: float = G_MIN
     dtype: str = "bf16"
     gate: str = "bounded"      # "bounded" (g_min applies) or "softplus" (no lower bound)
+    raw: bool = False          # q, k unnormalised and beta a logit (normalised in the operator)
 
     @property
     def T(self) -> int:
@@ -115,16 +116,21 @@ class PrefillInputs:
         return int(self.cu_seqlens.shape[0] - 1)
 
 
-def _draw_qkvzb(rng, T, H, d, dtype, z_mean=0.0, z_std=1.0):
-    q = _l2norm_last(rng.standard_normal((T, H, d), dtype=np.float32))
-    k = _l2norm_last(rng.standard_normal((T, H, d), dtype=np.float32))
+def _draw_qkvzb(rng, T, H, d, dtype, z_mean=0.0, z_std=1.0, raw=False):
+    """raw: q, k left unnormalised and beta left as its logit (the same draws)."""
+    q = rng.standard_normal((T, H, d), dtype=np.float32)
+    k = rng.standard_normal((T, H, d), dtype=np.float32)
+    if not raw:
+        q, k = _l2norm_last(q), _l2norm_last(k)
     v = rng.standard_normal((T, H, d), dtype=np.float32)
     z = rng.standard_normal((T, H, d), dtype=np.float32)
     if z_std != 1.0:
         z *= np.float32(z_std)
     if z_mean != 0.0:
         z += np.float32(z_mean)
-    beta = _sigmoid_f32(rng.standard_normal((T, H), dtype=np.float32))
+    beta = rng.standard_normal((T, H), dtype=np.float32)
+    if not raw:
+        beta = _sigmoid_f32(beta)
     return (_store(q, dtype), _store(k, dtype), _store(v, dtype), _store(z, dtype),
             _store(beta, dtype))
 
@@ -158,7 +164,7 @@ def make_prefill(seed: int, T: int, H: int, dtype: str = "bf16", *, A_std: float
                  lengths=None, varlen_total: Optional[int] = None, varlen_lo: int = 64,
                  varlen_hi: int = 16384, s0_std: float = 0.0, s0_docs: str = "first",
                  z_mean: float = 0.0, z_std: float = 1.0, d: int = D,
-                 gate: str = "bounded") -> PrefillInputs:
+                 gate: str = "bounded", raw: bool = False) -> PrefillInputs:
     """Generic prefill recipe.
 
     ``lengths`` gives explicit document lengths; ``varlen_total`` draws them
@@ -167,7 +173,7 @@ def make_prefill(seed: int, T: int, H: int, dtype: str = "bf16", *, A_std: float
     state ~ N(0, s0_std); other documents start from zero.
     """
     rng = np.random.default_rng(seed)
-    q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype, z_mean=z_mean, z_std=z_std)
+    q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype, z_mean=z_mean, z_std=z_std, raw=raw)
     A_log = (rng.standard_normal(H, dtype=np.float32) * np.float32(A_std)).astype(np.float32) \
         if A_std > 0 else np.zeros(H, dtype=np.float32)
     if lengths is not None:
@@ -194,7 +200,7 @@ def make_prefill(seed: int, T: int, H: int, dtype: str = "bf16", *, A_std: float
             S0[1:] = rng.standard_normal((n_docs_for_s0 - 1, H, d, d), dtype=np.float32) \
                 * np.float32(s0_std)
     return PrefillInputs(q=q, k=k, v=v, z=z, beta=beta, A_log=A_log, S0=S0,
-                         cu_seqlens=cu_from_lengths(lens), dtype=dtype, gate=gate)
+                         cu_seqlens=cu_from_lengths(lens), dtype=dtype, gate=gate, raw=raw)
 
 
 # ----------------------------------------------------------------------------
@@ -225,6 +231,7 @@ class DecodeInputs:
     wz: Optional[Tensor] = None
     wbeta: Optional[Tensor] = None  # [N, W2, H]
     W2: int = 0
+    raw: bool = False     # q, k unnormalised and beta a logit (normalised in the operator)
 
     @property
     def N(self) -> int:
@@ -237,14 +244,14 @@ class DecodeInputs:
 
 def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
                 A_std: float = 0.5, s_std: float = 0.02, d: int = D,
-                accepted=None, W2: int = 0) -> DecodeInputs:
+                accepted=None, W2: int = 0, raw: bool = False) -> DecodeInputs:
     """Decode-with-verify recipe: draft cache first (q,k,v,z,beta order), then A,
     the saved state, the accepted lengths U{0..W}, then the bonus token, then (if
     W2 > 0) the W2 drafts of the next window.  The draws of a call with W2 > 0
     start with exactly those of the same call with W2 = 0."""
     rng = np.random.default_rng(seed)
     T = N * W
-    q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype)
+    q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype, raw=raw)
     cq = Tensor(q.data.reshape(N, W, H, d), dtype)
     ck = Tensor(k.data.reshape(N, W, H, d), dtype)
     cv = Tensor(v.data.reshape(N, W, H, d), dtype)
@@ -258,10 +265,10 @@ def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
     else:
         acc = np.asarray(accepted, dtype=np.int32)
         assert acc.shape == (N,)
-    nq, nk, nv, nz, nb = _draw_qkvzb(rng, N, H, d, dtype)
+    nq, nk, nv, nz, nb = _draw_qkvzb(rng, N, H, d, dtype, raw=raw)
     win = {}
     if W2 > 0:
-        wq, wk, wv, wz, wb = _draw_qkvzb(rng, N * W2, H, d, dtype)
+        wq, wk, wv, wz, wb = _draw_qkvzb(rng, N * W2, H, d, dtype, raw=raw)
         win = dict(wq=Tensor(wq.data.reshape(N, W2, H, d), dtype),
                    wk=Tensor(wk.data.reshape(N, W2, H, d), dtype),
                    wv=Tensor(wv.data.reshape(N, W2, H, d), dtype),
@@ -269,7 +276,7 @@ def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
                    wbeta=Tensor(wb.data.reshape(N, W2, H), dtype), W2=W2)
     return DecodeInputs(state=state, cq=cq, ck=ck, cv=cv, cz=cz, cbeta=cb, accepted=acc,
                         nq=nq, nk=nk, nv=nv, nz=nz, nbeta=nb, A_log=A_log, W=W, dtype=dtype,
-                        **win)
+                        raw=raw, **win)
 
 
 # ----------------------------------------------------------------------------

@@ -13,6 +13,8 @@ Contents
     (M_t = (I - beta k k^T) Diag(alpha), segment pairs and their composition).
   * ``chunk_form.py``-- the chunkwise (UT-transform) form, fp64, used only to
     check that the chunked rewrite equals the recurrence.
+  * ``l2_normalize``, ``sigmoid``, ``operands`` (below) -- for raw inputs, the
+    q/k L2 normalisation and beta sigmoid that the operator then performs itself.
 
 Pins: see ``tests/test_oracle_pins.py``.  Every oracle function is pinned by
 at least one closed form, special case or independent formulation there.
@@ -99,6 +101,30 @@ def gate_softplus(z: np.ndarray, A_log: Optional[np.ndarray]) -> np.ndarray:
     return g
 
 
+def l2_normalize(x: np.ndarray) -> np.ndarray:
+    """x / ||x||_2 over the last axis (the channels of one token and head), fp64; a
+    zero vector stays zero.  The normalisation of q and k that the KDA kernels
+    perform in-kernel when given unnormalised inputs ("序列维度（下）", section on
+    which form each phase uses)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """1 / (1 + e^-x), fp64: beta from its logit (same section)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def operands(inp, q: np.ndarray, k: np.ndarray, beta: np.ndarray):
+    """(q, k, beta) as the recurrence takes them: unchanged, or, for inputs marked
+    raw, q and k L2-normalised per (token, head) and beta = sigmoid(logit)."""
+    if getattr(inp, "raw", False):
+        return l2_normalize(q), l2_normalize(k), sigmoid(beta)
+    return q, k, beta
+
+
 def gate_of(inp, z: np.ndarray, heads=None) -> np.ndarray:
     """The gate that ``inp`` names ("bounded": equation (5); "softplus": the
     unbounded Kimi Linear map) on logits z [T, H', dk] of heads ``heads``."""
@@ -143,11 +169,12 @@ def recurrent(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int = 0):
 
 
 def forward(inp, nthreads: int = 0):
-    """Full operator on a ``kda_gen.PrefillInputs``: gate, then the recurrence."""
+    """Full operator on a ``kda_gen.PrefillInputs``: gate (and, for raw inputs, the
+    q/k normalisation and beta sigmoid), then the recurrence."""
     g = gate_of(inp, inp.z.f64())
     S0 = None if inp.S0 is None else inp.S0.astype(np.float64)
-    return recurrent(inp.q.f64(), inp.k.f64(), inp.v.f64(), g, inp.beta.f64(), S0,
-                     inp.cu_seqlens, nthreads)
+    q, k, b = operands(inp, inp.q.f64(), inp.k.f64(), inp.beta.f64())
+    return recurrent(q, k, inp.v.f64(), g, b, S0, inp.cu_seqlens, nthreads)
 
 
 def decode(inp, nthreads: int = 0):
@@ -174,6 +201,7 @@ def decode(inp, nthreads: int = 0):
             cq[n, :a], ck[n, :a], cv[n, :a], cz[n, :a], cb[n, :a])
         q[s + a], k[s + a], v[s + a], z[s + a], b[s + a] = nq[n], nk[n], nv[n], nz[n], nb[n]
     g = gate(z, inp.A_log, inp.g_min)
+    q, k, b = operands(inp, q, k, b)
     o, S = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
     o_bonus = o[cu[1:] - 1]
     return o_bonus, S
@@ -209,6 +237,7 @@ def decode_window(inp, nthreads: int = 0):
                 pq[n, :m], pk[n, :m], pv[n, :m], pz[n, :m], pb[n, :m])
             s += m
     g = gate(z, inp.A_log, inp.g_min)
+    q, k, b = operands(inp, q, k, b)
     o, _ = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
     o_bonus = o[cu[:-1] + acc]
     o_window = np.stack([o[cu[n] + acc[n] + 1:cu[n + 1]] for n in range(N)])

@@ -61,9 +61,9 @@ def oracle_forward(inp, heads=None, group=8):
         hs = heads[g0:g0 + group]
         gg = oracle.gate_of(inp, _slice_f32(inp.z, hs).astype(np.float64), hs)
         S0 = None if inp.S0 is None else inp.S0[:, hs].astype(np.float64)
-        oo, SS = oracle.recurrent(_slice_f32(inp.q, hs), _slice_f32(inp.k, hs),
-                                  _slice_f32(inp.v, hs), gg, _slice_f32(inp.beta, hs), S0,
-                                  inp.cu_seqlens)
+        qq, kk, bb = oracle.operands(inp, _slice_f32(inp.q, hs), _slice_f32(inp.k, hs),
+                                     _slice_f32(inp.beta, hs))
+        oo, SS = oracle.recurrent(qq, kk, _slice_f32(inp.v, hs), gg, bb, S0, inp.cu_seqlens)
         o[:, g0:g0 + len(hs)] = oo
         S[:, g0:g0 + len(hs)] = SS
     return o, S
@@ -155,7 +155,8 @@ def oracle_checkpoints(inp, interval):
     """{(d, j): state after the first j * interval tokens of document d [H, dk, dv]}
     for every j >= 1 with j * interval < the document's length: the oracle's final
     state over that prefix of the document."""
-    g_all = oracle.gate(inp.z.f64(), inp.A_log, inp.g_min)
+    g_all = oracle.gate_of(inp, inp.z.f64())
+    q_all, k_all, b_all = oracle.operands(inp, inp.q.f64(), inp.k.f64(), inp.beta.f64())
     cu = inp.cu_seqlens
     out = {}
     for d in range(inp.N):
@@ -164,8 +165,8 @@ def oracle_checkpoints(inp, interval):
         j = 1
         while j * interval < b - a:
             e = a + j * interval
-            _, S = oracle.recurrent(inp.q.f64()[a:e], inp.k.f64()[a:e], inp.v.f64()[a:e],
-                                    g_all[a:e], inp.beta.f64()[a:e], S0)
+            _, S = oracle.recurrent(q_all[a:e], k_all[a:e], inp.v.f64()[a:e], g_all[a:e],
+                                    b_all[a:e], S0)
             out[(d, j)] = S[0]
             j += 1
     return out

@@ -11,6 +11,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -108,3 +109,30 @@ def test_mutant_fails_a_pin(tmp_path, name):
         oracle._lib = saved
         oracle._LIB_PATH = real_path
         oracle._SRC = os.path.join(os.path.dirname(real_path), "kda_oracle.c")
+
+
+# The raw-input preprocessing is NumPy code in oracle/__init__.py: mutate it by
+# substituting the functions, and check that a pin fails each time.
+RAW_PIN_TESTS = [pins.test_raw_inputs_scale_invariance, pins.test_raw_inputs_reduce_to_normalised,
+                 pins.test_raw_inputs_retrieval]
+RAW_MUTANTS = {
+    "normalise_by_squared_norm": ("l2_normalize",
+                                  lambda x: np.asarray(x, np.float64) /
+                                  np.maximum(np.sum(np.asarray(x, np.float64) ** 2, -1, keepdims=True), 1e-300)),
+    "no_normalisation": ("l2_normalize", lambda x: np.asarray(x, np.float64)),
+    "sigmoid_sign": ("sigmoid", lambda x: 1.0 / (1.0 + np.exp(np.asarray(x, np.float64)))),
+    "beta_logit_unchanged": ("sigmoid", lambda x: np.asarray(x, np.float64)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RAW_MUTANTS))
+def test_raw_mutant_fails_a_pin(name, monkeypatch):
+    attr, bad = RAW_MUTANTS[name]
+    monkeypatch.setattr(oracle, attr, bad)
+    failed = []
+    for t in RAW_PIN_TESTS:
+        try:
+            t(oracle)
+        except AssertionError:
+            failed.append(t.__name__)
+    assert failed, f"mutant {name} passed every pin"

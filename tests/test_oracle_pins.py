@@ -6,6 +6,7 @@ after the erase, the output read before the update, a transposed state, a
 wrong gate -- fails at least one of them.  No expected value here comes from
 the GPU path.
 """
+import dataclasses
 import json
 import math
 import os
@@ -336,6 +337,56 @@ def test_decode_window_equals_explicit_steps(oracle_mod):
     # the window's draws come after those of the plain recipe
     plain = kda_gen.make_decode(12, N=5, H=2, W=4, dtype="bf16", d=128, accepted=[0, 4, 1, 3, 2])
     assert np.array_equal(plain.state, inp.state) and np.array_equal(plain.nq.data, inp.nq.data)
+
+
+# ---------------------------------------------------------------------------
+# Raw inputs: q, k normalised and beta = sigmoid(logit) inside the operator
+# ("序列维度（下）", section on which form each phase uses: the kernels take q,
+# k and beta before L2 normalisation and sigmoid)
+# ---------------------------------------------------------------------------
+def _raw_case(seed, **kw):
+    return kda_gen.make_prefill(seed, 150, 2, "f32", raw=True, lengths=[90, 60], **kw)
+
+
+def test_raw_inputs_scale_invariance(oracle_mod):
+    """Only the direction of q and k counts: scaling each raw q and k row by its
+    own positive factor changes nothing."""
+    inp = _raw_case(21)
+    o, S = oracle_mod.forward(inp)
+    rng = _rng(21)
+    # powers of two, so that the scaled fp32 rows are exactly proportional
+    cq = np.exp2(rng.integers(-8, 9, size=inp.q.shape[:2] + (1,))).astype(np.float32)
+    ck = np.exp2(rng.integers(-8, 9, size=inp.k.shape[:2] + (1,))).astype(np.float32)
+    scaled = kda_gen.PrefillInputs(
+        kda_gen.Tensor(inp.q.data * cq, "f32"), kda_gen.Tensor(inp.k.data * ck, "f32"),
+        inp.v, inp.z, inp.beta, inp.A_log, inp.S0, inp.cu_seqlens, inp.g_min, "f32", raw=True)
+    o2, S2 = oracle_mod.forward(scaled)
+    assert _rel(o2, o) < 1e-12 and _rel(S2, S) < 1e-12
+
+
+def test_raw_inputs_reduce_to_normalised(oracle_mod):
+    """Rows already of unit norm and beta logits of 0 (sigmoid(0) = 1/2 exactly)
+    give the operator on those rows with beta = 1/2; zero rows give zero outputs."""
+    inp = kda_gen.make_prefill(22, 150, 2, "f32", lengths=[90, 60])   # unit rows (fp32)
+    half = np.full(inp.beta.shape, 0.5, dtype=np.float32)
+    plain = dataclasses.replace(inp, beta=kda_gen.Tensor(half, "f32"))
+    raw = dataclasses.replace(inp, beta=kda_gen.Tensor(np.zeros_like(half), "f32"), raw=True)
+    o1, S1 = oracle_mod.forward(plain)
+    o2, S2 = oracle_mod.forward(raw)
+    assert _rel(o2, o1) < 1e-6 and _rel(S2, S1) < 1e-6   # the fp32 rows are unit to ~1e-7
+    zq = dataclasses.replace(raw, q=kda_gen.Tensor(np.zeros_like(inp.q.data), "f32"))
+    o3, _ = oracle_mod.forward(zq)
+    assert np.all(o3 == 0)
+
+
+def test_raw_inputs_retrieval(oracle_mod):
+    """A large beta logit is beta = 1; with q = k (raw, any norm) the delta rule
+    then returns v at every step, as with unit keys and beta = 1."""
+    inp = _raw_case(23)
+    big = np.full(inp.beta.shape, 60.0, dtype=np.float32)
+    r = dataclasses.replace(inp, q=inp.k, beta=kda_gen.Tensor(big, "f32"))
+    o, _ = oracle_mod.forward(r)
+    assert np.max(np.abs(o - inp.v.f64())) < 1e-10
 
 
 # ---------------------------------------------------------------------------
