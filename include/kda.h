@@ -20,7 +20,19 @@
  *   * dtype selects the element type of q, k, v, g_logits, beta and o
  *     (KDA_F32 or KDA_BF16).  States are fp32 in every mode.
  *   * q and k are taken as given (callers L2-normalise them); beta is taken as
- *     given, already in (0,1).  The gate is applied inside the kernels.
+ *     given, already in (0,1).  The gate is applied inside the kernels.  With
+ *     KDA_RAW_INPUTS OR'ed into dtype, the kernels take q, k and beta one step
+ *     earlier, as the pages describe the KDA kernels doing
+ *     ("序列维度（下）", section on which form each phase uses): each (token,
+ *     head) row of q and of k is scaled to unit L2 norm (an all-zero row stays
+ *     zero) and beta is given as a logit, beta = Sigmoid(logit).  The bf16
+ *     prefill rounds the normalised q and k rows to bf16, the precision of all
+ *     its matrix operands; the decode step keeps them, and beta, in fp32.
+ *     Accepted by the bf16 two-kernel prefill (kda_chunk_fwd with a workspace,
+ *     kda_chunk_prep, kda_segment_scan with bf16 arithmetic,
+ *     kda_chunk_fwd_checkpoints, kda_chunk_fwd_unbounded) and by the decode
+ *     entry points; the fused and fp32-arithmetic prefill return
+ *     KDA_ERR_UNSUPPORTED.  kda_chunk_recurrence ignores it (it reads v only).
  *   * The caller owns every buffer, including workspaces.  The library never
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream).  Return codes describe
@@ -56,6 +68,8 @@ typedef enum kda_status {
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* Flag OR'ed into a dtype argument: q, k unnormalised and beta a logit (above). */
+#define KDA_RAW_INPUTS 0x100
 
 /* Arithmetic of the prefill paths.  KDA_COMPUTE_AUTO picks bf16 MFMA operands
  * with fp32 accumulation for bf16 inputs and fp32 MFMA for fp32 inputs;

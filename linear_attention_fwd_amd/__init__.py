@@ -5,6 +5,10 @@ behind the C ABI declared in ``include/kda.h``.  PyTorch provides device memory
 and the current stream.  There is no fallback: if the library is missing or the
 tensors are not on a GPU, calls raise.
 
+Every compute function takes ``raw_inputs=True`` for q, k not yet L2-normalised
+and beta given as a logit (the kernels then normalise and apply the sigmoid;
+KDA_RAW_INPUTS in the C ABI).
+
 Entry points (same names as the C ABI):
   * ``kda_chunk_fwd``    -- chunkwise prefill of packed documents
   * ``kda_chunk_fwd_unbounded`` -- the same with the unbounded (softplus) gate
@@ -24,6 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_RAW_INPUTS = 0x100  # OR'ed into dtype: q, k unnormalised and beta a logit
 KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
@@ -118,12 +123,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, raw_inputs: bool = False) -> int:
+    """dtype argument of the C ABI for tensor t, with KDA_RAW_INPUTS when q, k are
+    unnormalised and beta is a logit (the kernels normalise and apply the sigmoid)."""
     torch = _torch()
+    flag = KDA_RAW_INPUTS if raw_inputs else 0
     if t.dtype == torch.bfloat16:
-        return KDA_BF16
+        return KDA_BF16 | flag
     if t.dtype == torch.float32:
-        return KDA_F32
+        return KDA_F32 | flag
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -180,7 +188,8 @@ def kda_chunk_fwd_workspace_size(N: int, T: int, H: int, dk: int = 128, dv: int 
 def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                   initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, compute: int = KDA_COMPUTE_AUTO,
-                  o=None, final_state=None, workspace=None) -> Tuple[object, Optional[object]]:
+                  o=None, final_state=None, workspace=None,
+                  raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
     """Chunkwise KDA prefill.  q, k, v, g_logits: [T, H, 128]; beta: [T, H] (same
     dtype, bf16 or fp32); A_log: [H] fp32 or None; initial_state: [N, H, 128, 128]
     fp32 or None; cu_seqlens: [N+1] int32 (device and/or host copy).
@@ -205,7 +214,8 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                            float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
-                           dk, dv, _dtype_code(q), int(compute), _ptr(o), _ptr(final_state),
+                           dk, dv, _dtype_code(q, raw_inputs), int(compute), _ptr(o),
+                           _ptr(final_state),
                            ws_ptr, ws_bytes, _stream())
     _check(rc)
     return o, final_state
@@ -214,7 +224,7 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
 def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=None,
                             cu_seqlens=None, cu_seqlens_host=None,
                             output_final_state: bool = True, o=None, final_state=None,
-                            workspace=None) -> Tuple[object, Optional[object]]:
+                            workspace=None, raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
     """``kda_chunk_fwd`` with the unbounded gate g = -exp(A_h) softplus(z) (bf16
     inputs, two-kernel path).  Returns (o, final_state) as ``kda_chunk_fwd``."""
     torch = _torch()
@@ -231,7 +241,8 @@ def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=N
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_unbounded(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
                                      _ptr(A_log), _ptr(initial_state), _ptr(cu_dev), host_ptr, N,
-                                     T, H, dk, dv, _dtype_code(q), _ptr(o), _ptr(final_state),
+                                     T, H, dk, dv, _dtype_code(q, raw_inputs), _ptr(o),
+                                     _ptr(final_state),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream())
     _check(rc)
@@ -253,7 +264,8 @@ def checkpoint_index(cu_seqlens_host, d: int, j: int, interval: int) -> int:
 def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None,
                               g_min: float = -5.0, initial_state=None, cu_seqlens=None,
                               cu_seqlens_host=None, output_final_state: bool = True, o=None,
-                              final_state=None, checkpoints=None, workspace=None):
+                              final_state=None, checkpoints=None, workspace=None,
+                              raw_inputs: bool = False):
     """kda_chunk_fwd (two-kernel path, bf16) that also writes the state every
     ``interval`` tokens inside each document (see ``checkpoint_index``).
     Returns (o, final_state, checkpoints [kda_checkpoint_count, H, 128, 128] fp32)."""
@@ -274,7 +286,7 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_checkpoints(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log), float(g_min),
-        _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H, dk, dv, _dtype_code(q),
+        _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H, dk, dv, _dtype_code(q, raw_inputs),
         int(interval), _ptr(checkpoints), checkpoints.numel() * checkpoints.element_size(),
         _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream())
@@ -283,7 +295,7 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
 
 
 def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -5.0,
-                   cu_seqlens=None, cu_seqlens_host=None) -> None:
+                   cu_seqlens=None, cu_seqlens_host=None, raw_inputs: bool = False) -> None:
     """First half of the two-kernel prefill: writes every (head, chunk) image into
     ``workspace`` (uint8, kda_chunk_fwd_workspace_size bytes).  bf16 inputs only."""
     lib = load_library()
@@ -292,7 +304,7 @@ def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     _check(lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(cu_dev), host_ptr, N, T, H, dk, dv,
-                              _dtype_code(q), _ptr(workspace),
+                              _dtype_code(q, raw_inputs), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream()))
 
 
@@ -338,7 +350,7 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                      initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                      n_segments: int = 0, output_final_state: bool = True,
                      compute: int = KDA_COMPUTE_AUTO, workspace=None, o=None,
-                     final_state=None):
+                     final_state=None, raw_inputs: bool = False):
     """Prefill via per-segment affine pairs, an on-device pair scan and a re-run
     from exact entry states.  Same tensors as ``kda_chunk_fwd``; n_segments <= 0
     uses one segment per compute unit.  Returns (o, final_state)."""
@@ -357,7 +369,7 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_segment_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
-                              dk, dv, _dtype_code(q), int(compute), int(n_seg), _ptr(o),
+                              dk, dv, _dtype_code(q, raw_inputs), int(compute), int(n_seg), _ptr(o),
                               _ptr(final_state), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream())
     _check(rc)
@@ -365,7 +377,8 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
 
 
 def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
-                    A_log=None, g_min: float = -5.0, state_slots=None, o=None, err_flag=None):
+                    A_log=None, g_min: float = -5.0, state_slots=None, o=None, err_flag=None,
+                    raw_inputs: bool = False):
     """One decode step with speculative-verify replay, updating ``state`` in place.
 
     state: [S_pool, H, 128, 128] fp32; cq, ck, cv, cz: [N, W, H, 128]; cbeta: [N, W, H];
@@ -389,14 +402,15 @@ def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbet
     rc = lib.kda_decode_step(_ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
                              _ptr(cz), _ptr(cbeta), _ptr(accepted), int(W), _ptr(nq), _ptr(nk),
                              _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(A_log), float(g_min), _ptr(o),
-                             _ptr(err_flag), N, H, d, d, _dtype_code(nq), _stream())
+                             _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())
     _check(rc)
     return o
 
 
 def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
                            wq, wk, wv, wz, wbeta, A_log=None, g_min: float = -5.0,
-                           state_slots=None, o=None, o_window=None, err_flag=None):
+                           state_slots=None, o=None, o_window=None, err_flag=None,
+                           raw_inputs: bool = False):
     """``kda_decode_step`` followed, in the same kernel, by the next draft window.
 
     Arguments as for ``kda_decode_step`` plus wq, wk, wv, wz: [N, W2, H, 128] and
@@ -432,12 +446,12 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
         _ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
         _ptr(accepted), int(W), _ptr(nq), _ptr(nk), _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(wq),
         _ptr(wk), _ptr(wv), _ptr(wz), _ptr(wbeta), int(W2), _ptr(A_log), float(g_min), _ptr(o),
-        _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq), _stream())
+        _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())
     _check(rc)
     return o, o_window
 
 
-__all__ = ["kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
+__all__ = ["KDA_RAW_INPUTS", "kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_decode_step_window",
            "kda_chunk_fwd_unbounded", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count", "load_library", "KDAError",
            "KDA_COMPUTE_AUTO", "KDA_COMPUTE_F32"]

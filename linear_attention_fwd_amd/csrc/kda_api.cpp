@@ -31,6 +31,16 @@ int hip_fail(hipError_t e, const char *what) {
 constexpr int kD = 128;
 constexpr int kC = 64;  // chunk length
 
+// The KDA_RAW_INPUTS flag of a dtype argument; the element type is the rest.
+bool take_raw_flag(int32_t &dtype) {
+  const bool raw = (dtype & KDA_RAW_INPUTS) != 0;
+  dtype &= ~KDA_RAW_INPUTS;
+  return raw;
+}
+int raw_unsupported(const char *who) {
+  return fail(KDA_ERR_UNSUPPORTED, "%s: KDA_RAW_INPUTS needs the bf16 two-kernel path", who);
+}
+
 // Sizes, dtype and document offsets shared by the prefill entry points.
 int check_layout(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N, int64_t T,
                  int32_t H, int32_t dk, int32_t dv, int32_t dtype) {
@@ -200,19 +210,22 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                   const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
                   int32_t dk, int32_t dv, int32_t dtype, int32_t compute, void *o,
                   float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool raw = take_raw_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
                          dk, dv, dtype, compute, o);
   if (rc != KDA_OK) return rc;
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   const bool split = workspace != nullptr && !f32c;
+  if (raw && !split) return raw_unsupported("kda_chunk_fwd");
   if (split) {
     rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
     if (rc != KDA_OK) return rc;
   }
   hipStream_t st = (hipStream_t)stream;
   if (T > 0 && split) {
-    const kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
-                                            cu_seqlens, N, T, H, o, final_state, workspace);
+    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
+                                      cu_seqlens, N, T, H, o, final_state, workspace);
+    p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
@@ -247,6 +260,7 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
                               float *checkpoints, size_t checkpoint_bytes, void *o,
                               float *final_state, void *workspace, size_t workspace_bytes,
                               void *stream) {
+  const bool raw = take_raw_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
                          dk, dv, dtype, KDA_COMPUTE_AUTO, o);
   if (rc != KDA_OK) return rc;
@@ -265,6 +279,7 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
                                       cu_seqlens, N, T, H, o, final_state, workspace);
     p.ckpt = checkpoints;
     p.ckpt_chunks = interval / kC;
+    p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_checkpoints launch");
@@ -283,6 +298,7 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
                             float *final_state, void *workspace, size_t workspace_bytes,
                             void *stream) {
   const float unused_g_min = -5.0f;  // the unbounded gate takes no g_min
+  const bool raw = take_raw_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, unused_g_min, cu_seqlens, cu_seqlens_host, N, T,
                          H, dk, dv, dtype, KDA_COMPUTE_AUTO, o);
   if (rc != KDA_OK) return rc;
@@ -295,6 +311,7 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, unused_g_min, initial_state,
                                       cu_seqlens, N, T, H, o, final_state, workspace);
     p.gate = kda::GATE_SOFTPLUS;
+    p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
@@ -316,6 +333,7 @@ int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const voi
                    const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
                    int32_t dv, int32_t dtype, void *workspace, size_t workspace_bytes,
                    void *stream) {
+  const bool raw = take_raw_flag(dtype);
   if (T > 0 && (!q || !k || !g_logits || !beta))
     return fail(KDA_ERR_NULL, "q, k, g_logits and beta must be non-NULL when T > 0");
   int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
@@ -324,8 +342,9 @@ int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const voi
   if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prep takes bf16 inputs only");
   rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
   if (rc != KDA_OK || T == 0) return rc;
-  const kda::SplitParams p = split_params(q, k, nullptr, g_logits, beta, A_log, g_min, nullptr,
-                                          cu_seqlens, N, T, H, nullptr, nullptr, workspace);
+  kda::SplitParams p = split_params(q, k, nullptr, g_logits, beta, A_log, g_min, nullptr,
+                                    cu_seqlens, N, T, H, nullptr, nullptr, workspace);
+  p.raw = raw;
   hipError_t e = kda::launch_chunk_prep(p, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_chunk_prep launch");
 }
@@ -335,6 +354,7 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
                          int32_t dk, int32_t dv, int32_t dtype, const void *workspace,
                          size_t workspace_bytes, void *o, float *final_state, void *stream) {
   if (T > 0 && (!v || !o)) return fail(KDA_ERR_NULL, "v and o must be non-NULL when T > 0");
+  take_raw_flag(dtype);  // v is never normalised: the flag changes nothing here
   int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
   if (rc != KDA_OK) return rc;
   if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_recurrence takes bf16 inputs only");
@@ -385,18 +405,20 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
                      int32_t dk, int32_t dv, int32_t dtype, int32_t compute,
                      int32_t n_segments, void *o, float *final_state, void *workspace,
                      size_t workspace_bytes, void *stream) {
+  const bool raw = take_raw_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
                          dk, dv, dtype, compute, o);
   if (rc != KDA_OK) return rc;
   if (final_state && initial_state && final_state == initial_state)
     return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not alias initial_state");
+  const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
+  if (raw && f32c) return raw_unsupported("kda_segment_scan");
   int64_t req = n_segments;
   if (req <= 0) {
     const int cus = kda_default_segments();
     if (cus < 0) return cus;
     req = cus;
   }
-  const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   hipStream_t st = (hipStream_t)stream;
   if (T > 0 && !f32c) {
     // two-kernel path: chunk prep over all chunks, segment pairs and the re-run
@@ -424,6 +446,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     p.n_seg = (int)sp.n_seg;
     p.seg_slots = sp.len;
     p.pairs = pairs;
+    p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan prep");
     p.rmode = 2;  // A: segment pairs; resets at document starts are folded into them
@@ -508,6 +531,7 @@ static int decode_common(float *state, const int32_t *state_slots, const void *c
                          const kda::DecodeWindowArgs &win, const float *A_log, float g_min,
                          void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
                          int32_t dv, int32_t dtype, void *stream, const char *who) {
+  const bool raw = take_raw_flag(dtype);
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
   if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
     return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");
@@ -525,9 +549,10 @@ static int decode_common(float *state, const int32_t *state_slots, const void *c
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = (dtype == KDA_BF16)
       ? kda::launch_decode<kda::bf16_t>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq,
-                                        nk, nv, nz, nbeta, win, A_log, g_min, o, err_flag, N, H, st)
+                                        nk, nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N,
+                                        H, st)
       : kda::launch_decode<float>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk,
-                                  nv, nz, nbeta, win, A_log, g_min, o, err_flag, N, H, st);
+                                  nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N, H, st);
   if (e != hipSuccess) return hip_fail(e, who);
   return KDA_OK;
 }

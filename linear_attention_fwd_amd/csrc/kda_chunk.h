@@ -209,15 +209,40 @@ struct PrepLds {
   float wtot[4][D];   // per-wave cumulative-sum totals
 };
 
+// Raw inputs: q or k of this thread's 4 tokens (8 channels each) scaled to unit
+// L2 norm per token and rounded back to bf16, the precision every matrix
+// operand built from them has; the 16 lanes of a token group (lane bits 0-3)
+// hold the 128 channels of its tokens.  An all-zero row (a padding row) stays
+// zero.
+__device__ __forceinline__ void l2norm_rows(bufio<bf16_t>::raw8 (&R)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x[8];
+    bufio<bf16_t>::cvt8(R[r], x);
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(x[c], x[c], ss);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 8);
+    const float sc = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+    const bf16x8 y = to_bf16x8(floatx8{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc, x[4] * sc,
+                                       x[5] * sc, x[6] * sc, x[7] * sc});
+    R[r].a = __builtin_bit_cast(u32x4, y);
+  }
+}
+
 // a1: gate and inclusive cumulative sum over the chunk (base 2).  Tokens at or
 // beyond len are padding: no decay.  Leaves G[r][c] for this thread's tokens
 // and channels, beta, Gref and GC2 in LDS (and Gend for the unbounded gate);
-// ends with a barrier.  UNB selects the unbounded gate (gmin2 unused).
+// ends with a barrier.  UNB selects the unbounded gate (gmin2 unused);
+// beta_logit takes beta as a logit (raw inputs: beta = sigmoid(logit), fp32).
 template <class IO, bool UNB = false>
 __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO::raw8 (&Rz)[4],
                                                  typename IO::raw1 Rb, float c1, float gmin2,
                                                  int len, int tid, int w, int tq, int cg,
-                                                 float (&G)[4][8]) {
+                                                 float (&G)[4][8], bool beta_logit = false) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool tok = 16 * w + 4 * tq + r < len;
@@ -229,7 +254,10 @@ __device__ __forceinline__ void prep_gate_cumsum(PrepLds &ps, const typename IO:
     for (int c = 0; c < 8; ++c)
       G[r][c] = UNB ? kda_gate2_softplus(zz[c], cm) : kda_gate2(zz[c], c1, gm);
   }
-  if (tid < CH) ps.beta[tid] = IO::cvt1(Rb);
+  if (tid < CH) {
+    const float b = IO::cvt1(Rb);
+    ps.beta[tid] = beta_logit ? __builtin_amdgcn_rcpf(1.0f + __expf(-b)) : b;
+  }
   // in-lane over r, across the 4 token groups of the wave (lanes 16 apart),
   // then across waves
 #pragma unroll

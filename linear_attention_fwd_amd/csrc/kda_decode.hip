@@ -34,7 +34,9 @@ template <typename Tin> struct DecodeWindow {
 };
 constexpr int DEC_TOKBATCH = 8;  // tokens staged in LDS at a time
 
-template <typename Tin>
+
+// RAW: q, k unnormalised and beta a logit (normalised and sigmoid applied here)
+template <typename Tin, bool RAW>
 __global__ void __launch_bounds__(DEC_THREADS)
 kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                   const Tin *__restrict__ cq, const Tin *__restrict__ ck,
@@ -46,6 +48,7 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                   const float *__restrict__ A_log, float g_min, Tin *__restrict__ o,
                   int32_t *__restrict__ err_flag, int H) {
   __shared__ __align__(16) float s_k[DEC_TOKBATCH][D];
+  __shared__ float s_qsc[DEC_TOKBATCH], s_ksc[DEC_TOKBATCH];  // raw inputs: 1 / ||q||, 1 / ||k||
   __shared__ __align__(16) float s_q[DEC_TOKBATCH][D];
   __shared__ __align__(16) float s_a[DEC_TOKBATCH][D];
   __shared__ __align__(16) float s_v[DEC_TOKBATCH][D];
@@ -116,11 +119,29 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
     }
     if (tid < nb) {
       const int t = t0 + tid;
-      s_b[tid] = (t < acc)    ? io<Tin>::load1(cbeta + ((int64_t)n * W + t) * H + h)
-                 : (t == acc) ? io<Tin>::load1(nbeta + (int64_t)n * H + h)
-                              : io<Tin>::load1(win.beta + ((int64_t)n * win.W2 + (t - acc - 1)) * H + h);
+      const float b = (t < acc)    ? io<Tin>::load1(cbeta + ((int64_t)n * W + t) * H + h)
+                      : (t == acc) ? io<Tin>::load1(nbeta + (int64_t)n * H + h)
+                                   : io<Tin>::load1(win.beta + ((int64_t)n * win.W2 + (t - acc - 1)) * H + h);
+      s_b[tid] = RAW ? __builtin_amdgcn_rcpf(1.0f + __expf(-b)) : b;  // fp32, like the rest
     }
     __syncthreads();
+    if constexpr (RAW) {  // L2 norms of q and k: wave w takes tokens w and w + 4 of the batch
+      for (int tt = wave; tt < nb; tt += 4) {
+        const float q0 = s_q[tt][lane], q1 = s_q[tt][lane + 64];
+        const float k0 = s_k[tt][lane], k1 = s_k[tt][lane + 64];
+        float sq = q0 * q0 + q1 * q1, sk = k0 * k0 + k1 * k1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          sq += __shfl_xor(sq, m);
+          sk += __shfl_xor(sk, m);
+        }
+        if (lane == 0) {
+          s_qsc[tt] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+          s_ksc[tt] = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+        }
+      }
+      __syncthreads();
+    }
 
     for (int tt = 0; tt < nb; ++tt) {
       const int t = t0 + tt;
@@ -131,6 +152,11 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
         const float4 k4 = *reinterpret_cast<const float4 *>(&s_k[tt][row0 + i]);
         aa[i] = a4.x; aa[i + 1] = a4.y; aa[i + 2] = a4.z; aa[i + 3] = a4.w;
         kk[i] = k4.x; kk[i + 1] = k4.y; kk[i + 2] = k4.z; kk[i + 3] = k4.w;
+      }
+      if constexpr (RAW) {
+        const float sc = s_ksc[tt];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kk[i] *= sc;
       }
       // decay, then the erase term against the decayed state
       float p[4] = {0.f, 0.f, 0.f, 0.f};
@@ -166,6 +192,11 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
         for (int i = 0; i < 16; i += 4) {
           const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][row0 + i]);
           qq[i] = q4.x; qq[i + 1] = q4.y; qq[i + 2] = q4.z; qq[i + 3] = q4.w;
+        }
+        if constexpr (RAW) {
+          const float sc = s_qsc[tt];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) qq[i] *= sc;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -204,16 +235,16 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const void *cv, const void *cz, const void *cbeta,
                          const int32_t *accepted, int W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
-                         const DecodeWindowArgs &w, const float *A_log, float g_min, void *o,
-                         int32_t *err_flag, int N, int H, hipStream_t stream) {
+                         const DecodeWindowArgs &w, bool raw, const float *A_log, float g_min,
+                         void *o, int32_t *err_flag, int N, int H, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)N * H));
   DecodeWindow<Tin> win{w.W2, (const Tin *)w.q, (const Tin *)w.k, (const Tin *)w.v,
                         (const Tin *)w.z, (const Tin *)w.beta, (Tin *)w.o};
-  hipLaunchKernelGGL(kda_decode_kernel<Tin>, grid, dim3(DEC_THREADS), 0, stream, state, slots,
-                     (const Tin *)cq, (const Tin *)ck, (const Tin *)cv, (const Tin *)cz,
-                     (const Tin *)cbeta, accepted, W, (const Tin *)nq, (const Tin *)nk,
-                     (const Tin *)nv, (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min,
-                     (Tin *)o, err_flag, H);
+  auto kernel = raw ? kda_decode_kernel<Tin, true> : kda_decode_kernel<Tin, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(DEC_THREADS), 0, stream, state, slots, (const Tin *)cq,
+                     (const Tin *)ck, (const Tin *)cv, (const Tin *)cz, (const Tin *)cbeta,
+                     accepted, W, (const Tin *)nq, (const Tin *)nk, (const Tin *)nv,
+                     (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min, (Tin *)o, err_flag, H);
   return hipGetLastError();
 }
 
@@ -221,13 +252,13 @@ template hipError_t launch_decode<float>(float *, const int32_t *, const void *,
                                          const void *, const void *, const void *,
                                          const int32_t *, int, const void *, const void *,
                                          const void *, const void *, const void *,
-                                         const DecodeWindowArgs &, const float *, float, void *,
-                                         int32_t *, int, int, hipStream_t);
+                                         const DecodeWindowArgs &, bool, const float *, float,
+                                         void *, int32_t *, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(float *, const int32_t *, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const int32_t *, int, const void *, const void *,
                                           const void *, const void *, const void *,
-                                          const DecodeWindowArgs &, const float *, float, void *,
-                                          int32_t *, int, int, hipStream_t);
+                                          const DecodeWindowArgs &, bool, const float *, float,
+                                          void *, int32_t *, int, int, hipStream_t);
 
 }  // namespace kda

@@ -71,6 +71,9 @@ struct SplitParams {
   // gate map: GATE_BOUNDED (g_min * sigmoid) or GATE_SOFTPLUS (unbounded,
   // g_min unused); only the prep kernel depends on it
   int gate;
+  // raw inputs: the prep kernel L2-normalises q and k and applies the sigmoid
+  // to beta
+  int raw;
 };
 constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
 size_t split_workspace_bytes(int64_t T, int N, int H);
@@ -116,7 +119,8 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const void *cv, const void *cz, const void *cbeta,
                          const int32_t *accepted, int W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
-                         const DecodeWindowArgs &win, const float *A_log, float g_min, void *o,
-                         int32_t *err_flag, int N, int H, hipStream_t stream);
+                         const DecodeWindowArgs &win, bool raw, const float *A_log,
+                         float g_min, void *o, int32_t *err_flag, int N, int H,
+                         hipStream_t stream);
 
 }  // namespace kda

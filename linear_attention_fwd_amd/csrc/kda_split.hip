@@ -88,8 +88,9 @@ static_assert(3 * sizeof(PrepSmem) <= 160 * 1024, "three prep workgroups per com
 
 // UNB: the unbounded Kimi Linear gate; the diagonal subtiles of M_qk and L are
 // then formed per position (prep_diag_positions) and the off-diagonal ones
-// with the key side referenced to the end of its subtile.
-template <bool UNB>
+// with the key side referenced to the end of its subtile.  RAW: q, k
+// unnormalised and beta a logit (normalised and sigmoid applied here).
+template <bool UNB, bool RAW>
 __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitParams p) {
   using Ar = Arith<false>;
   using IO = bufio<bf16_t>;
@@ -145,8 +146,12 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
     Rb = IO::ld1(rb, lane * H * ES);
   }
 
+  if constexpr (RAW) {  // q and k rows to unit L2 norm
+    l2norm_rows(Rq);
+    l2norm_rows(Rk);
+  }
   float G[4][8];
-  prep_gate_cumsum<IO, UNB>(sm.ps, Rz, Rb, c1, gmin2, len, tid, w, tq, cg, G);  // two barriers
+  prep_gate_cumsum<IO, UNB>(sm.ps, Rz, Rb, c1, gmin2, len, tid, w, tq, cg, G, RAW);  // two barriers
 
   const __amdgpu_buffer_rsrc_t ri =
       make_rsrc((char *)p.ws + ((int64_t)h * p.n_slots + slot) * IMG_BYTES, IMG_BYTES);
@@ -671,12 +676,16 @@ size_t split_workspace_bytes(int64_t T, int N, int H) {
 
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
   const int64_t blocks = p.n_slots * p.H;
-  if (p.gate == GATE_SOFTPLUS)
-    hipLaunchKernelGGL(kda_chunk_prep_kernel<true>, dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
-                       stream, p);
+  const dim3 grid((unsigned)blocks), block(FWD_THREADS);
+  const bool unb = p.gate == GATE_SOFTPLUS;
+  if (unb && p.raw)
+    hipLaunchKernelGGL((kda_chunk_prep_kernel<true, true>), grid, block, 0, stream, p);
+  else if (unb)
+    hipLaunchKernelGGL((kda_chunk_prep_kernel<true, false>), grid, block, 0, stream, p);
+  else if (p.raw)
+    hipLaunchKernelGGL((kda_chunk_prep_kernel<false, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(kda_chunk_prep_kernel<false>, dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
-                       stream, p);
+    hipLaunchKernelGGL((kda_chunk_prep_kernel<false, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

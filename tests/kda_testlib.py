@@ -87,7 +87,7 @@ def gpu_chunk_fwd(inp, compute=0, t=None, fused=False):
     t = t or gpu_inputs(inp)
     o, S = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min,
                              t["S0"], t["cu"], t["cu_host"], compute=compute,
-                             workspace=False if fused else None)
+                             workspace=False if fused else None, raw_inputs=inp.raw)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 
@@ -98,7 +98,7 @@ def gpu_chunk_fwd_unbounded(inp, t=None):
     import torch
     t = t or gpu_inputs(inp)
     o, S = kda.kda_chunk_fwd_unbounded(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
-                                       t["S0"], t["cu"], t["cu_host"])
+                                       t["S0"], t["cu"], t["cu_host"], raw_inputs=inp.raw)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 
@@ -109,7 +109,7 @@ def gpu_segment_scan(inp, n_segments=0, compute=0, t=None):
     t = t or gpu_inputs(inp)
     o, S = kda.kda_segment_scan(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
                                 inp.g_min, t["S0"], t["cu"], t["cu_host"],
-                                n_segments=n_segments, compute=compute)
+                                n_segments=n_segments, compute=compute, raw_inputs=inp.raw)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 
@@ -133,7 +133,8 @@ def gpu_decode(inp, t=None, state_slots=None, err_flag=None):
     t = t or decode_gpu_inputs(inp)
     o = kda.kda_decode_step(t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"],
                             t["accepted"], t["nq"], t["nk"], t["nv"], t["nz"], t["nbeta"],
-                            t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
+                            t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag,
+                            raw_inputs=inp.raw)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(t["state"])
 
@@ -146,7 +147,7 @@ def gpu_decode_window(inp, t=None, state_slots=None, err_flag=None):
     o, ow = kda.kda_decode_step_window(
         t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"], t["accepted"], t["nq"],
         t["nk"], t["nv"], t["nz"], t["nbeta"], t["wq"], t["wk"], t["wv"], t["wz"], t["wbeta"],
-        t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag)
+        t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag, raw_inputs=inp.raw)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(ow), kda_gen.from_torch(t["state"])
 

@@ -218,6 +218,28 @@ def test_decode_validation(lib):
     assert lib.kda_last_error() is not None
 
 
+def test_raw_inputs_flag(lib):
+    """KDA_RAW_INPUTS is accepted where the two-kernel prep or the decode kernel
+    runs and refused on the fused and fp32 prefill; other bits are unknown."""
+    RAW = kda.KDA_RAW_INPUTS
+    def fwd(dtype, ws, compute=0):
+        return lib.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1,
+                                 256, 4, 128, 128, dtype, compute, FAKE, None, ws,
+                                 1 << 30 if ws else 0, None)
+    assert fwd(1 | RAW, None) == KDA_ERR_UNSUPPORTED         # fused path (no workspace)
+    assert fwd(1 | RAW, FAKE, compute=1) == KDA_ERR_UNSUPPORTED  # fp32 arithmetic
+    assert fwd(0 | RAW, FAKE) == KDA_ERR_UNSUPPORTED         # fp32 inputs
+    assert fwd(1 | 0x200, FAKE) == KDA_ERR_DTYPE              # unknown bit
+    for n_seg in (0, 7):  # refused before the device is asked for its compute units
+        assert lib.kda_segment_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1,
+                                    256, 4, 128, 128, 1 | RAW, 1, n_seg, FAKE, None, FAKE, 1 << 30,
+                                    None) == KDA_ERR_UNSUPPORTED
+    # accepted by decode (rejected here only for the missing state)
+    assert lib.kda_decode_step(None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, None, -5.0, FAKE, None, 8, 4, 128, 128, 1 | RAW,
+                               None) == KDA_ERR_NULL
+
+
 def test_unbounded_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, T=256, H=4, dtype=1, ws=FAKE, ws_bytes=1 << 30)

@@ -326,6 +326,57 @@ def test_unbounded_gate_matches_oracle(name):
 
 
 # ---------------------------------------------------------------------------
+# raw inputs: q, k normalised and beta = sigmoid(logit) in the kernels
+# ---------------------------------------------------------------------------
+def _zero_rows(t, rows):
+    t.data[rows] = 0
+    return t
+
+
+@pytest.mark.parametrize("path", ["chunk_fwd", "segment_scan", "unbounded"])
+def test_raw_inputs_prefill(path):
+    """Unnormalised q, k and beta logits through the two-kernel prefill (and the
+    segment scan and the unbounded gate, which share its prep), against the
+    oracle that normalises them.  Some tokens have all-zero q or k rows (their
+    normalised rows stay zero)."""
+    inp = kda_gen.make_prefill(64, 1200, 4, "bf16", lengths=[500, 0, 77, 623], s0_std=0.05,
+                               s0_docs="all", raw=True,
+                               gate="softplus" if path == "unbounded" else "bounded")
+    _zero_rows(inp.q, [3, 600, 1199])
+    _zero_rows(inp.k, [4, 577, 1000])
+    _case(inp, 0)
+    print(f"    raw inputs, {path}", flush=True)
+    o_ref, S_ref = oracle_forward(inp)
+    if path == "chunk_fwd":
+        o, S = gpu_chunk_fwd(inp)
+    elif path == "segment_scan":
+        o, S = gpu_segment_scan(inp, n_segments=7)
+    else:
+        o, S = gpu_chunk_fwd_unbounded(inp)
+    assert np.all(o[[3, 600, 1199]] == 0)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_raw_inputs_decode_window(dtype):
+    """Raw draft, bonus and next-window inputs through the decode kernel."""
+    inp = kda_gen.make_decode(65, N=24, H=4, W=4, dtype=dtype,
+                              accepted=[i % 5 for i in range(24)], W2=3, raw=True)
+    print(f"[case] raw decode window N={inp.N} H={inp.H} dtype={dtype}", flush=True)
+    o_ref, ow_ref, S_ref = oracle.decode_window(inp)
+    o, ow, S = gpu_decode_window(inp)
+    o1, S1 = gpu_decode(inp)
+    assert np.array_equal(o, o1) and np.array_equal(S, S1)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    ew = max(rel_l2_slices(ow[:, j][:, :, None], ow_ref[:, j][:, :, None], axis_tokens=False)[0]
+             for j in range(3))
+    print(f"    o: {eo:.3e}  window: {ew:.3e}  state: {es:.3e}", flush=True)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert eo <= tol and ew <= tol and es <= tol
+
+
+# ---------------------------------------------------------------------------
 # decode with speculative-verify replay
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
