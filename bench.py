@@ -296,6 +296,24 @@ def main():
     torch.cuda.synchronize()
     unb_ms = float(np.mean([a.elapsed_time(c) for a, c in unb_ev]))
 
+    # ---------------- the same step on raw inputs (q, k normalised and the beta
+    # sigmoid applied in the kernels; the inputs here are already normalised,
+    # which changes nothing in the work done)
+    def raw_step():
+        kda.kda_chunk_fwd(q, k, v, z, b, A_log, inp.g_min, o=o, final_state=fin, workspace=ws,
+                          raw_inputs=True)
+
+    for _ in range(args.warmup):
+        raw_step()
+    torch.cuda.synchronize()
+    raw_ev = _events(torch, stream, args.steps)
+    for i in range(args.steps):
+        raw_ev[i][0].record(stream)
+        raw_step()
+        raw_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    raw_ms = float(np.mean([a.elapsed_time(c) for a, c in raw_ev]))
+
     # ---------------- decode with speculative verify -------------------------
     # the decode workload (N=512, H=96, 4 drafts + bonus) plus, drawn after it, a
     # next window of 4 drafts for the fused replay + bonus + window step
@@ -345,6 +363,22 @@ def main():
         win_ev[i][1].record(stream)
     torch.cuda.synchronize()
     win_ms = float(np.mean([a.elapsed_time(c) for a, c in win_ev]))
+
+    def raw_dstep():
+        kda.kda_decode_step(d_state, dt["cq"], dt["ck"], dt["cv"], dt["cz"], dt["cbeta"], d_acc,
+                            dt["nq"], dt["nk"], dt["nv"], dt["nz"], dt["nbeta"], d_A, dec.g_min,
+                            o=d_o, raw_inputs=True)
+
+    for _ in range(args.warmup):
+        raw_dstep()
+    torch.cuda.synchronize()
+    rawd_ev = _events(torch, stream, args.decode_steps)
+    for i in range(args.decode_steps):
+        rawd_ev[i][0].record(stream)
+        raw_dstep()
+        rawd_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    rawd_ms = float(np.mean([a.elapsed_time(c) for a, c in rawd_ev]))
 
     # ---------------- CPU oracle baseline (host cores of this machine) -----------
     cpu = None
@@ -398,6 +432,9 @@ def main():
         "unbounded_gate": {"gate": "-exp(A) softplus(z), diagonal subtiles per position in fp32",
                            "kernels_ms": unb_ms, "extra_ms": unb_ms - step_kernel_ms,
                            "tokens_per_s": T / (unb_ms * 1e-3)},
+        "raw_inputs": {"what": "q, k L2-normalised and beta sigmoid in the kernels",
+                       "prefill_kernels_ms": raw_ms, "prefill_extra_ms": raw_ms - step_kernel_ms,
+                       "decode_kernel_ms": rawd_ms, "decode_extra_ms": rawd_ms - dec_ms},
         "checkpoints": {"interval_tokens": interval, "kernels_ms": ck_ms,
                         "extra_ms": ck_ms - step_kernel_ms, "state_bytes_written": ck_written},
         "decode": {"workload": "N=512 H=96, 4 drafts + bonus, accepted U{0..4}, fp32 state",
