@@ -307,6 +307,42 @@ UNBOUNDED_CASES = {
 }
 
 
+def test_unbounded_gate_single_token_and_empty_document():
+    """The unbounded gate on a one-token document beside an empty one and a
+    ragged 70-token one: partial chunks pad with zeros, the empty document passes
+    its initial state through."""
+    inp = kda_gen.make_prefill(63, 71, 2, "bf16", lengths=[1, 0, 70], s0_std=0.05,
+                               s0_docs="all", gate="softplus")
+    _case(inp, 0)
+    o, S = gpu_chunk_fwd_unbounded(inp)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+    assert np.array_equal(S[1], inp.S0[1])
+
+
+def test_all_documents_empty():
+    """T = 0: nothing to run, every final state is the document's initial state
+    (chunk kernels, segment scan and the unbounded gate)."""
+    import torch
+    import linear_attention_fwd_amd as kda
+    H = 2
+    S0 = np.random.default_rng(67).standard_normal((3, H, 128, 128)).astype(np.float32)
+    z = torch.zeros((0, H, 128), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((0, H), dtype=torch.bfloat16, device="cuda")
+    s0 = torch.from_numpy(S0).cuda()
+    cu_host = np.zeros(4, dtype=np.int32)
+    cu = torch.from_numpy(cu_host).cuda()
+    print("[case] T=0, 3 empty documents", flush=True)
+    for name, call in (
+            ("chunk_fwd", lambda: kda.kda_chunk_fwd(z, z, z, z, b, None, -5.0, s0, cu, cu_host)),
+            ("segment_scan", lambda: kda.kda_segment_scan(z, z, z, z, b, None, -5.0, s0, cu, cu_host,
+                                                          n_segments=4)),
+            ("unbounded", lambda: kda.kda_chunk_fwd_unbounded(z, z, z, z, b, None, s0, cu, cu_host))):
+        o, S = call()
+        torch.cuda.synchronize()
+        assert o.shape == (0, H, 128)
+        assert np.array_equal(kda_gen.from_torch(S), S0), name
+
+
 @pytest.mark.parametrize("name", sorted(UNBOUNDED_CASES))
 def test_unbounded_gate_matches_oracle(name):
     c = dict(UNBOUNDED_CASES[name])
@@ -472,6 +508,25 @@ def test_decode_window_slots_and_empty_window():
     assert ow0.shape == (inp.N, 0, inp.H, 128)
     assert np.array_equal(kda_gen.from_torch(o0), o1)
     assert np.array_equal(kda_gen.from_torch(t0["state"]), S1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_without_drafts(dtype):
+    """W = 0: no draft cache at all, the step is the bonus token alone (with and
+    without a next window)."""
+    inp = kda_gen.make_decode(66, N=9, H=3, W=0, dtype=dtype, W2=2)
+    print(f"[case] decode without drafts N={inp.N} H={inp.H} dtype={dtype}", flush=True)
+    o_ref, S_ref = oracle.decode(inp)
+    o, S = gpu_decode(inp)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    assert es <= TOL_F32 and eo <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    _, ow_ref, _ = oracle.decode_window(inp)
+    o2, ow, S2 = gpu_decode_window(inp)
+    assert np.array_equal(o2, o) and np.array_equal(S2, S)
+    ew = max(rel_l2_slices(ow[:, j][:, :, None], ow_ref[:, j][:, :, None], axis_tokens=False)[0]
+             for j in range(2))
+    assert ew <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
 def test_decode_equals_chunk_fwd_on_the_same_tokens():
