@@ -191,6 +191,9 @@ CHECKPOINT_CASES = {
                         s0_std=0.02, s0_docs="all"), 128),
     "single_doc_512": (dict(seed=48, T=2048, H=2, dtype="bf16", z_mean=-6.0, s0_std=0.05,
                             s0_docs="all"), 512),
+    # every chunk boundary, raw inputs (normalised in the prep kernel)
+    "every_chunk_raw_64": (dict(seed=68, T=900, H=2, dtype="bf16", lengths=[64, 65, 771],
+                                s0_std=0.05, s0_docs="all", raw=True), 64),
 }
 
 
@@ -211,7 +214,8 @@ def test_checkpoints_match_oracle(name):
     t = gpu_inputs(inp)
     o1, S1 = gpu_chunk_fwd(inp, t=t)
     o2, S2, ck = kda.kda_chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["z"], t["beta"], interval,
-                                               t["A_log"], inp.g_min, t["S0"], t["cu"], t["cu_host"])
+                                               t["A_log"], inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                               raw_inputs=inp.raw)
     torch.cuda.synchronize()
     assert np.array_equal(o1, kda_gen.from_torch(o2)) and np.array_equal(S1, kda_gen.from_torch(S2))
     ck = kda_gen.from_torch(ck)

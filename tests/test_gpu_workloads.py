@@ -163,3 +163,28 @@ def test_decode_window_workload():
     es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
     print(f"[decode window] window o max {ew:.3e} | state max {es:.3e}", flush=True)
     assert ew <= TOL_BF16 and es <= TOL_F32
+
+
+def test_raw_inputs_workloads():
+    """The single-sequence and decode workloads drawn raw (q, k unnormalised, beta
+    logits, from the same draws), normalised inside the kernels, against the
+    oracle that normalises them (sampled heads for the prefill)."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    pre = kda_gen.make_prefill(1, 8192, 96, "bf16", A_std=0.5, raw=True)
+    print("[case] raw inputs, T=8192 H=96 and decode N=512 H=96", flush=True)
+    t = gpu_inputs(pre)
+    o, S = gpu_chunk_fwd(pre, t=t)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    heads = list(range(3, 96, 12))
+    o_ref, S_ref = oracle_forward(pre, heads=heads, group=8)
+    eo, es = _report("raw prefill, 8 sampled heads", o[:, heads], o_ref, S[:, heads], S_ref,
+                     pre.cu_seqlens)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    dec = kda_gen.make_decode(4, 512, 96, 4, "bf16", raw=True)
+    od_ref, Sd_ref = oracle.decode(dec)
+    od, Sd = gpu_decode(dec)
+    e1, _ = rel_l2_slices(od[:, :, None], od_ref[:, :, None], axis_tokens=False)
+    e2, _ = rel_l2_slices(Sd, Sd_ref, axis_tokens=False)
+    print(f"[raw decode] o max {e1:.3e} | state max {e2:.3e}", flush=True)
+    assert e1 <= TOL_BF16 and e2 <= TOL_F32
