@@ -121,7 +121,9 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
 
 /* Workspace bytes kda_chunk_fwd's two-kernel path needs for N documents of T
  * tokens in total and H heads: one 62 KiB image per head and chunk slot,
- * (floor(T / 64) + N) slots per head.  0 for invalid sizes. */
+ * (floor(T / 64) + N) slots per head, then 4 bytes per document (rounded up to
+ * 256) for the order in which the recurrence takes the documents (longest
+ * first; the order does not change any result).  0 for invalid sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv);
 
 /* The two halves of kda_chunk_fwd's two-kernel path, callable on their own
@@ -135,8 +137,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk,
  *
  * kda_chunk_recurrence: the serial chunk recurrence of every (document, head)
  * over the images kda_chunk_prep wrote for the same q, k, g_logits, beta,
- * A_log, g_min and cu_seqlens; reads v and initial_state, writes o and
- * final_state (which may alias initial_state).  The workspace must not be
+ * A_log, g_min and cu_seqlens (device and host copies); reads v and
+ * initial_state, writes o and final_state (which may alias initial_state).
+ * kda_chunk_prep also writes the document order the recurrence reads (see
+ * kda_chunk_fwd_workspace_size).  The workspace must not be
  * modified in between; both calls must be on the same stream (or ordered). */
 int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const void *beta,
                    const float *A_log, float g_min, const int32_t *cu_seqlens,

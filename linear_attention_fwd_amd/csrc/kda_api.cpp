@@ -99,16 +99,33 @@ int check_image_workspace(const void *workspace, size_t workspace_bytes, int64_t
   return KDA_OK;
 }
 
+// The recurrence takes the documents longest first (an order the prep kernel
+// launcher writes into the workspace) unless their chunk counts already do
+// not increase, when the order would be the input order.
+bool needs_doc_order(const int32_t *cu_host, int32_t N) {
+  if (!cu_host || N < 2) return false;
+  int64_t prev = INT64_MAX;
+  for (int32_t d = 0; d < N; ++d) {
+    const int64_t c = ((int64_t)cu_host[d + 1] - cu_host[d] + kC - 1) / kC;
+    if (c > prev) return true;
+    prev = c;
+  }
+  return false;
+}
+
 kda::SplitParams split_params(const void *q, const void *k, const void *v, const void *g_logits,
                               const void *beta, const float *A_log, float g_min,
-                              const float *initial_state, const int32_t *cu_seqlens, int32_t N,
-                              int64_t T, int32_t H, void *o, float *final_state, const void *ws) {
+                              const float *initial_state, const int32_t *cu_seqlens,
+                              const int32_t *cu_host, int32_t N, int64_t T, int32_t H, void *o,
+                              float *final_state, const void *ws) {
   kda::SplitParams p{};
   p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
   p.A_log = A_log; p.g_min = g_min;
   p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
   p.init = initial_state; p.o = o; p.final_state = final_state;
   p.ws = const_cast<void *>(ws); p.n_slots = kda::n_chunk_slots(T, N);
+  if (needs_doc_order(cu_host, N))
+    p.order = (int32_t *)((char *)p.ws + kda::split_order_offset(T, N, H));
   return p;
 }
 
@@ -224,7 +241,8 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
   hipStream_t st = (hipStream_t)stream;
   if (T > 0 && split) {
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
-                                      cu_seqlens, N, T, H, o, final_state, workspace);
+                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
+                                      workspace);
     p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
@@ -276,7 +294,8 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
   hipStream_t st = (hipStream_t)stream;
   if (T > 0) {
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
-                                      cu_seqlens, N, T, H, o, final_state, workspace);
+                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
+                                      workspace);
     p.ckpt = checkpoints;
     p.ckpt_chunks = interval / kC;
     p.raw = raw;
@@ -309,7 +328,8 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
   hipStream_t st = (hipStream_t)stream;
   if (T > 0) {
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, unused_g_min, initial_state,
-                                      cu_seqlens, N, T, H, o, final_state, workspace);
+                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
+                                      workspace);
     p.gate = kda::GATE_SOFTPLUS;
     p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
@@ -343,7 +363,8 @@ int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const voi
   rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
   if (rc != KDA_OK || T == 0) return rc;
   kda::SplitParams p = split_params(q, k, nullptr, g_logits, beta, A_log, g_min, nullptr,
-                                    cu_seqlens, N, T, H, nullptr, nullptr, workspace);
+                                    cu_seqlens, cu_seqlens_host, N, T, H, nullptr, nullptr,
+                                    workspace);
   p.raw = raw;
   hipError_t e = kda::launch_chunk_prep(p, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_chunk_prep launch");
@@ -363,8 +384,8 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
   hipStream_t st = (hipStream_t)stream;
   if (T > 0) {
     const kda::SplitParams p = split_params(nullptr, nullptr, v, nullptr, nullptr, nullptr, -5.0f,
-                                            initial_state, cu_seqlens, N, T, H, o, final_state,
-                                            workspace);
+                                            initial_state, cu_seqlens, cu_seqlens_host, N, T, H,
+                                            o, final_state, workspace);
     hipError_t e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_recurrence launch");
   }
@@ -442,7 +463,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     float *gentry = gpairs + (size_t)g_max * H * kD * 2 * kD;
 
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
-                                      cu_seqlens, N, T, H, o, final_state, workspace);
+                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
+                                      workspace);
+    p.order = nullptr;  // segments, not documents
     p.n_seg = (int)sp.n_seg;
     p.seg_slots = sp.len;
     p.pairs = pairs;

@@ -74,9 +74,16 @@ struct SplitParams {
   // raw inputs: the prep kernel L2-normalises q and k and applies the sigmoid
   // to beta
   int raw;
+  // mode 0: the order in which the recurrence takes the documents (longest
+  // first), [N] in the workspace after the images, written by launch_chunk_prep;
+  // nullptr = input order
+  int32_t *order;
 };
 constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
+// chunk images [H, n_slots, image], then the document order (4 N bytes,
+// rounded up to 256)
 size_t split_workspace_bytes(int64_t T, int N, int H);
+size_t split_order_offset(int64_t T, int N, int H);
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);
 

@@ -478,7 +478,8 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   const int split = rest % nsplit;
   const int unit = (rest / nsplit) * 8 + xlo;
   if (unit >= units) return;
-  const int item = unit / p.H;
+  // documents in the order the prep wrote (longest first), else input order
+  const int item = uni(p.rmode == 0 && p.order ? (int)cu_load(p.order, unit / p.H) : unit / p.H);
   const int h = unit % p.H;
   int64_t s_begin, s_end;
   if (p.rmode == 0) {
@@ -670,11 +671,102 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
   }
 }
 
-size_t split_workspace_bytes(int64_t T, int N, int H) {
+// ---------------------------------------------------------------------------
+// The order in which the recurrence takes the documents.  Each (document,
+// head) unit holds its workgroups for the document's whole chunk chain, and
+// workgroups start in index order as compute units free up, so a long
+// document that starts late ends late: with units in input order the step
+// takes up to (total chunks / CUs) + longest chain, in longest-first order
+// about the larger of the two.  Documents are sorted by decreasing chunk count
+// rounded down to its leading 4 bits (a 256-bucket key, empty documents last);
+// equal keys keep their input order, so the order is a fixed permutation of
+// [0, N) whatever the timing.  One workgroup: a histogram pass, a scan of the
+// buckets, and a placement pass that ranks equal keys with wave ballots.
+// ---------------------------------------------------------------------------
+constexpr int ORDER_THREADS = 256;
+constexpr int ORDER_WAVES = ORDER_THREADS / 64;
+
+// 0 for the most chunks ... 254 for one chunk; 255 for an empty document
+__device__ __forceinline__ int order_key(const int32_t *cu, int d) {
+  const int64_t a = cu[d], b = cu[d + 1];
+  if (b <= a) return 255;
+  const uint64_t c = (uint64_t)((b - a + CH - 1) / CH);
+  const int e = 63 - __builtin_clzll(c);
+  const int m = e >= 3 ? (int)((c >> (e - 3)) & 7) : (int)((c << (3 - e)) & 7);
+  return 254 - min(8 * e + m, 254);
+}
+
+__global__ void __launch_bounds__(ORDER_THREADS) kda_doc_order_kernel(const int32_t *cu, int N,
+                                                                        int32_t *order) {
+  __shared__ int base[256];
+  __shared__ int cnt[ORDER_WAVES][256];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  base[t] = 0;
+  __syncthreads();
+  for (int d = t; d < N; d += ORDER_THREADS) atomicAdd(&base[order_key(cu, d)], 1);
+  __syncthreads();
+  if (w == 0) {  // exclusive scan of the histogram, four buckets per lane
+    int v[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = base[4 * lane + i]; s += v[i]; }
+    int inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int run = inc - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { base[4 * lane + i] = run; run += v[i]; }
+  }
+  __syncthreads();
+  for (int d0 = 0; d0 < N; d0 += ORDER_THREADS) {
+#pragma unroll
+    for (int i = 0; i < ORDER_WAVES; ++i) cnt[i][t] = 0;
+    __syncthreads();
+    const int d = d0 + t;
+    const bool valid = d < N;
+    const int k = valid ? order_key(cu, d) : 0;
+    // lanes of this wave with the same key: the intersection over the key's
+    // 8 bits of the lanes that agree on that bit
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (k >> bit) & 1;
+      const uint64_t ones = __ballot(valid && on);
+      same &= on ? ones : ~ones;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1));
+    if (valid && rank == 0) cnt[w][k] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int pos = base[k] + rank;
+      for (int i = 0; i < w; ++i) pos += cnt[i][k];
+      order[pos] = d;
+    }
+    __syncthreads();
+    int add = 0;
+#pragma unroll
+    for (int i = 0; i < ORDER_WAVES; ++i) add += cnt[i][t];
+    base[t] += add;
+    __syncthreads();
+  }
+}
+
+size_t split_order_offset(int64_t T, int N, int H) {
   return (size_t)n_chunk_slots(T, N) * (size_t)H * (size_t)IMG_BYTES;
+}
+size_t split_workspace_bytes(int64_t T, int N, int H) {
+  return split_order_offset(T, N, H) + ((size_t)N * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {
+  if (p.order) {
+    hipLaunchKernelGGL(kda_doc_order_kernel, dim3(1), dim3(ORDER_THREADS), 0, stream, p.cu, p.N,
+                       p.order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t blocks = p.n_slots * p.H;
   const dim3 grid((unsigned)blocks), block(FWD_THREADS);
   const bool unb = p.gate == GATE_SOFTPLUS;

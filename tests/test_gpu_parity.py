@@ -106,6 +106,80 @@ def test_prep_then_recurrence_equals_chunk_fwd():
     assert np.array_equal(S1, kda_gen.from_torch(S2))
 
 
+def _expected_doc_order(lengths):
+    """Longest first by chunk count rounded down to its leading 4 bits, empty
+    documents last, input order among equal keys."""
+    def key(n):
+        c = (n + 63) // 64
+        if c == 0:
+            return 255
+        e = c.bit_length() - 1
+        m = (c >> (e - 3)) & 7 if e >= 3 else (c << (3 - e)) & 7
+        return 254 - min(8 * e + m, 254)
+    return sorted(range(len(lengths)), key=lambda d: (key(lengths[d]), d))
+
+
+@pytest.mark.parametrize("case", ["unsorted_with_empty", "many_documents", "sorted"])
+def test_document_order(case):
+    """kda_chunk_prep writes the order in which the recurrence takes the
+    documents after the chunk images: longest first, a permutation of [0, N);
+    documents already in that order leave it unwritten."""
+    import torch
+    import linear_attention_fwd_amd as kda
+    from kda_testlib import gpu_inputs
+    rng = np.random.default_rng(36)
+    lengths = {"unsorted_with_empty": [5, 0, 130, 64, 1, 200, 0, 4000, 65],
+               "many_documents": [int(x) for x in rng.integers(0, 300, size=700)] + [0, 9000],
+               "sorted": [900, 640, 577, 64, 10, 0]}[case]
+    inp = kda_gen.make_prefill(36, int(sum(lengths)), 1, "bf16", lengths=lengths)
+    _case(inp, 0)
+    t = gpu_inputs(inp)
+    nbytes = kda.kda_chunk_fwd_workspace_size(inp.N, inp.T, inp.H)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    kda.kda_chunk_prep(t["q"], t["k"], t["z"], t["beta"], ws, t["A_log"], inp.g_min, t["cu"],
+                       t["cu_host"])
+    torch.cuda.synchronize()
+    off = (inp.T // 64 + inp.N) * inp.H * 63488
+    assert nbytes == off + (4 * inp.N + 255) // 256 * 256
+    order = ws[off:off + 4 * inp.N].cpu().numpy().view(np.int32)
+    if case == "sorted":
+        assert np.all(order == -1)
+        return
+    assert np.array_equal(np.sort(order), np.arange(inp.N))
+    assert order.tolist() == _expected_doc_order(lengths)
+
+
+def test_document_order_changes_no_result():
+    """Hundreds of documents around two long ones (the order kernel places
+    them over two passes) through the whole prefill, against the oracle; and
+    the same documents packed in another order (already longest first, so no
+    order is written) give bit-identical results per document.  Lengths start
+    at 40 tokens: the max over (document, head) slices of a few tokens each
+    samples the far tail of bf16 operand rounding on outputs that cancel."""
+    rng = np.random.default_rng(37)
+    lengths = [int(x) for x in rng.integers(40, 120, size=300)]
+    lengths[17], lengths[250] = 2000, 700
+    lengths[5] = lengths[100] = 0
+    inp = kda_gen.make_prefill(37, int(sum(lengths)), 2, "bf16", lengths=lengths, s0_std=0.02,
+                               s0_docs="all")
+    _case(inp, 0)
+    o, S = gpu_chunk_fwd(inp)
+    _check_prefill(inp, o, S, _tols(inp, 0))
+    cu = inp.cu_seqlens
+    perm = sorted(range(inp.N), key=lambda d: -((lengths[d] + 63) // 64))
+    cu2 = np.concatenate([[0], np.cumsum([lengths[d] for d in perm])]).astype(np.int32)
+
+    def packed(x):
+        return np.concatenate([x[cu[d]:cu[d + 1]] for d in perm])
+    inp2 = kda_gen.PrefillInputs(*(kda_gen.Tensor(packed(x.data), x.dtype) for x in
+                                   (inp.q, inp.k, inp.v, inp.z, inp.beta)), inp.A_log,
+                                 inp.S0[perm], cu2, inp.g_min, inp.dtype)
+    o2, S2 = gpu_chunk_fwd(inp2)
+    for i, d in enumerate(perm):
+        assert np.array_equal(o2[cu2[i]:cu2[i + 1]], o[cu[d]:cu[d + 1]]), d
+    assert np.array_equal(S2, S[perm])
+
+
 def test_chunk_fwd_is_deterministic():
     inp = kda_gen.make_prefill(31, 500, 4, "bf16", s0_std=0.02, s0_docs="all")
     o1, S1 = gpu_chunk_fwd(inp)
