@@ -429,7 +429,8 @@ def main():
                               "bytes": floor_bytes,
                               "GBps": floor_bytes / (step_kernel_ms * 1e-3) / 1e9,
                               "frac": floor_bytes / (step_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-        "unbounded_gate": {"gate": "-exp(A) softplus(z), diagonal subtiles per position in fp32",
+        "unbounded_gate": {"gate": "-exp(A) softplus(z); diagonal subtiles on MFMA where their "
+                                   "decay range allows, else per position in fp32",
                            "kernels_ms": unb_ms, "extra_ms": unb_ms - step_kernel_ms,
                            "tokens_per_s": T / (unb_ms * 1e-3)},
         "raw_inputs": {"what": "q, k L2-normalised and beta sigmoid in the kernels",

@@ -206,8 +206,25 @@ struct PrepLds {
   float Gend[4][D];   // G (base 2) at the last token of each subtile (unbounded gate)
   float F[6][D];      // e^(Gref[I] - Gref[J]) for I > J
   float beta[CH];
-  float wtot[4][D];   // per-wave cumulative-sum totals
+  union {
+    float wtot[4][D];  // per-wave cumulative-sum totals (a1 only)
+    float Fd[4][D];    // unbounded gate: e^(Gref[I] - Gend[I]), the diagonal subtiles' factor
+  };
 };
+
+// Unbounded gate: diagonal subtile I takes the two-factor MFMA form of the
+// bounded gate when, in every channel, its decay over the subtile G_s - G_e
+// (base 2) is at most DIAG_RANGE2.  That is inside the range the bounded gate
+// guarantees (15 steps of at most 5 / ln 2), so the factors e^(G_i - G_s) and
+// e^(G_s - G_j) neither underflow nor overflow, as there.  Wave-uniform; needs
+// Gref and Gend (after prep_gate_cumsum).
+constexpr float DIAG_RANGE2 = 100.0f;
+__device__ __forceinline__ bool diag_two_factor(const PrepLds &ps, int I) {
+  const int lane = threadIdx.x & 63;
+  const float r0 = ps.Gref[I][lane] - ps.Gend[I][lane];
+  const float r1 = ps.Gref[I][lane + 64] - ps.Gend[I][lane + 64];
+  return __ballot(!(r0 <= DIAG_RANGE2 && r1 <= DIAG_RANGE2)) == 0;  // a NaN range fails too
+}
 
 // Raw inputs: q or k of this thread's 4 tokens (8 channels each) scaled to unit
 // L2 norm per token and rounded back to bf16, the precision every matrix
@@ -374,11 +391,18 @@ __device__ __forceinline__ void prep_decay_operands(const PrepLds &ps, typename 
 
 // F[pair][c] = e^(Gref[I][c] - Gref[J][c]) (UNB: e^(Gref[I][c] - Gend[J][c]) <= 1),
 // pairs (1,0),(2,0),(2,1),(3,0),(3,1),(3,2): moves the key side's reference to
-// the first token of the query subtile
+// the first token of the query subtile.  UNB also gives the diagonal subtiles
+// Fd[I][c] = e^(Gref[I][c] - Gend[I][c]) >= 1 (clamped below fp32 overflow; it
+// is used only where diag_two_factor holds).  Ends before a barrier: wtot,
+// which Fd overlays, is dead once prep_gate_cumsum has returned.
 template <bool UNB = false>
 __device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
-  for (int x = tid; x < 6 * D; x += FWD_THREADS) {
+  for (int x = tid; x < (UNB ? 10 : 6) * D; x += FWD_THREADS) {
     const int pi = x / D, c = x % D;
+    if (UNB && pi >= 6) {
+      ps.Fd[pi - 6][c] = __builtin_amdgcn_exp2f(fminf(ps.Gref[pi - 6][c] - ps.Gend[pi - 6][c], 126.0f));
+      continue;
+    }
     const int I = (pi == 0) ? 1 : (pi < 3 ? 2 : 3);
     const int J = (pi == 0) ? 0 : (pi < 3 ? pi - 1 : pi - 3);
     ps.F[pi][c] = __builtin_amdgcn_exp2f(ps.Gref[I][c] - (UNB ? ps.Gend[J][c] : ps.Gref[J][c]));
@@ -390,10 +414,12 @@ __device__ __forceinline__ void prep_pair_factors(PrepLds &ps, int tid) {
 // with row j of the pair's tile at columns 4g..4g+3 and writes them at once.
 // L (natural order, operand precision) goes to LDS; M_qk goes to
 // mqk_sink(row, J, mq[4]).  PRODUCTS selects M_qk (1), L (2) or both (3); a
-// product not selected reads nothing from its tile (Qh or Kh).  SKIP_DIAG
-// leaves the diagonal pairs (I = J) to prep_diag_positions.
+// product not selected reads nothing from its tile (Qh or Kh).  UNB: the key
+// side is referenced to the end of its subtile; a diagonal pair takes the
+// factor Fd where diag_two_factor holds and is left to prep_diag_positions
+// otherwise.
 constexpr int PROD_MQK = 1, PROD_L = 2;
-template <class Ar, int PRODUCTS, bool SKIP_DIAG = false, class MqkSink>
+template <class Ar, int PRODUCTS, bool UNB = false, class MqkSink>
 __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const typename Ar::E *Qh,
                                                       const typename Ar::E *Kh,
                                                       const typename Ar::E *Ki, typename Ar::E *L,
@@ -403,13 +429,14 @@ __device__ __forceinline__ void prep_subtile_products(const PrepLds &ps, const t
   for (int pidx = w; pidx < 10; pidx += 4) {
     const int I = (pidx == 0) ? 0 : (pidx < 3 ? 1 : (pidx < 6 ? 2 : 3));
     const int J = pidx - I * (I + 1) / 2;
-    if (SKIP_DIAG && I == J) continue;
+    if (UNB && I == J && !diag_two_factor(ps, I)) continue;
     floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       BReg kin;  // key side of subtile J, referenced to the first token of subtile I
       if (I == J) {
-        kin = Ar::template breg_lds<D>(Ki, 16 * J + j, kb, g);
+        kin = UNB ? Ar::template breg_lds_scaled<D>(Ki, 16 * J + j, kb, g, ps.Fd[I])
+                  : Ar::template breg_lds<D>(Ki, 16 * J + j, kb, g);
       } else {
         const int fp = I * (I - 1) / 2 + J;
         kin = Ar::template breg_lds_scaled<D>(Ki, 16 * J + j, kb, g, ps.F[fp]);
@@ -457,10 +484,11 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// a3 on the diagonal subtiles when the gate has no lower bound: subtile I = w
-// (this wave's own 16 tokens) from the definition, one position pair at a time
-// in fp32, the path that the bound removes ("序列维度（下）", section on the
-// 16-token subtiles): for j <= i in the subtile
+// a3 on the diagonal subtiles when the gate has no lower bound and the
+// subtile's decay range is too wide for two factors (diag_two_factor fails):
+// subtile I = w (this wave's own 16 tokens) from the definition, one position
+// pair at a time in fp32, the path that the bound removes ("序列维度（下）",
+// section on the 16-token subtiles): for j <= i in the subtile
 //   M_qk[i][j] = sum_c q_ic k_jc e^(G_ic - G_jc),
 //   L[i][j]    = beta_i sum_c k_ic k_jc e^(G_ic - G_jc)   (j < i only),
 // where e^(G_ic - G_jc) <= 1 never overflows.  The wave stages its tokens'

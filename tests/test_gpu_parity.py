@@ -382,6 +382,10 @@ UNBOUNDED_CASES = {
     # can form its diagonal block; documents with initial states, a ragged tail
     "strong_decay_varlen": dict(seed=62, T=1500, H=4, lengths=[700, 13, 64, 723], z_mean=2.0,
                                 z_std=3.0, A_std=1.0, s0_std=0.05, s0_docs="all"),
+    # about -4.5 per step: the diagonal subtiles' decay ranges straddle the
+    # limit of the two-factor MFMA form (100 in base 2), so it runs right at
+    # its edge, beside per-position subtiles in the same chunks
+    "two_factor_limit": dict(seed=64, T=640, H=4, z_mean=4.4, z_std=0.3, A_std=0.0),
 }
 
 
@@ -421,15 +425,36 @@ def test_all_documents_empty():
         assert np.array_equal(kda_gen.from_torch(S), S0), name
 
 
+def _diagonal_subtile_forms(inp):
+    """(subtile-heads whose decay range G_s - G_e stays within 100 in base 2
+    in every channel, those beyond it), from the oracle's gate: the kernels
+    form the first kind's diagonal block with two MFMA factors, the second
+    per position."""
+    g = oracle.gate_softplus(inp.z.f64(), inp.A_log)
+    cu = inp.cu_seqlens
+    within = beyond = 0
+    for d in range(inp.N):
+        for c0 in range(cu[d], cu[d + 1], 64):
+            for s0 in range(c0, min(c0 + 64, cu[d + 1]), 16):
+                decay = -g[s0 + 1:min(s0 + 16, cu[d + 1])].sum(axis=0) / np.log(2.0)
+                ok = (decay <= 100.0).all(axis=-1)
+                within += int(ok.sum())
+                beyond += int((~ok).sum())
+    return within, beyond
+
+
 @pytest.mark.parametrize("name", sorted(UNBOUNDED_CASES))
 def test_unbounded_gate_matches_oracle(name):
     c = dict(UNBOUNDED_CASES[name])
     seed, T, H = c.pop("seed"), c.pop("T"), c.pop("H")
     inp = kda_gen.make_prefill(seed, T, H, "bf16", gate="softplus", **c)
     print(f"[case] unbounded gate {name} T={T} H={H} N={inp.N}", flush=True)
+    within, beyond = _diagonal_subtile_forms(inp)
+    print(f"    diagonal subtile-heads: {within} two-factor, {beyond} per position", flush=True)
     if name == "strong_decay_varlen":
         G = np.cumsum(oracle.gate_softplus(inp.z.f64()[:16], inp.A_log), axis=0)
         assert (G[0] - G[15]).max() > 100.0  # e^100 is beyond fp32
+    assert within > 0 and (beyond > 0) == (name != "single_ragged_1000")
     o_ref, S_ref = oracle_forward(inp)
     o, S = gpu_chunk_fwd_unbounded(inp)
     assert np.isfinite(o).all() and np.isfinite(S).all()
