@@ -125,6 +125,17 @@ def measured_traffic(here: str, kernel: str):
     return None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _events(torch, stream, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n)]
@@ -392,7 +403,7 @@ def main():
         cpu_s = time.perf_counter() - t1
         # the whole workload (all heads, all tokens); the scale factor below is then 1
         cpu = {"value": T / (cpu_s * H / len(heads)), "unit": "tokens/s",
-               "cores": oracle.max_threads(), "kind": "oracle",
+               "cores": oracle.max_threads(), "kind": "oracle", "cpu_model": _cpu_model(),
                "sample": f"fp64 token recurrence (gate precomputed) over the whole workload: "
                          f"{len(heads)} heads x {T} tokens, {cpu_s:.2f} s wall"}
 

@@ -214,11 +214,14 @@ struct PrepLds {
 
 // Unbounded gate: diagonal subtile I takes the two-factor MFMA form of the
 // bounded gate when, in every channel, its decay over the subtile G_s - G_e
-// (base 2) is at most DIAG_RANGE2.  That is inside the range the bounded gate
-// guarantees (15 steps of at most 5 / ln 2), so the factors e^(G_i - G_s) and
-// e^(G_s - G_j) neither underflow nor overflow, as there.  Wave-uniform; needs
-// Gref and Gend (after prep_gate_cumsum).
-constexpr float DIAG_RANGE2 = 100.0f;
+// (base 2) is at most DIAG_RANGE2.  The key operand e^(G_s - G_j) k_j then
+// stays below 2^116 |k_j| (no overflow) and the query operand e^(G_i - G_s) q_i
+// above 2^-116 |q_i|: only query elements under 2^-10 can drop below the
+// smallest normal float, in the last tokens of the widest channels, where
+// their terms are under 0.1% of a unit-norm entry.  (The bounded gate's own
+// range is at most 15 * 5 / ln 2 = 108.)  Wave-uniform; needs Gref and Gend
+// (after prep_gate_cumsum).
+constexpr float DIAG_RANGE2 = 116.0f;
 __device__ __forceinline__ bool diag_two_factor(const PrepLds &ps, int I) {
   const int lane = threadIdx.x & 63;
   const float r0 = ps.Gref[I][lane] - ps.Gend[I][lane];
