@@ -391,7 +391,7 @@ def main():
     torch.cuda.synchronize()
     rawd_ms = float(np.mean([a.elapsed_time(c) for a, c in rawd_ev]))
 
-    # ---------------- CPU oracle baseline (host cores of this machine) -----------
+    # ---------------- CPU oracle baseline (this machine's host cores) --------
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
