@@ -202,7 +202,7 @@ def other_workload(args, np, torch, kda_gen, kda, dev):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (got --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
         return 2
     if args.copy_calibration:
