@@ -119,7 +119,7 @@ def _expected_doc_order(lengths):
     return sorted(range(len(lengths)), key=lambda d: (key(lengths[d]), d))
 
 
-@pytest.mark.parametrize("case", ["unsorted_with_empty", "many_documents", "sorted"])
+@pytest.mark.parametrize("case", ["unsorted_with_empty", "many_documents", "mostly_empty", "sorted"])
 def test_document_order(case):
     """kda_chunk_prep writes the order in which the recurrence takes the
     documents after the chunk images: longest first, a permutation of [0, N);
@@ -130,6 +130,7 @@ def test_document_order(case):
     rng = np.random.default_rng(36)
     lengths = {"unsorted_with_empty": [5, 0, 130, 64, 1, 200, 0, 4000, 65],
                "many_documents": [int(x) for x in rng.integers(0, 300, size=700)] + [0, 9000],
+               "mostly_empty": [0] * 300 + [500] + [0] * 213,
                "sorted": [900, 640, 577, 64, 10, 0]}[case]
     inp = kda_gen.make_prefill(36, int(sum(lengths)), 1, "bf16", lengths=lengths)
     _case(inp, 0)
