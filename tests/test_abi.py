@@ -289,3 +289,18 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([__import__("sys").executable, "-c", code], capture_output=True,
                          text=True, cwd=ROOT, check=True).stdout
     assert out.strip() == "1", out
+
+
+@pytest.mark.parametrize("lang,std", [("c", "c99"), ("c++", "c++11")])
+def test_header_is_plain_c(lang, std, tmp_path):
+    """include/kda.h compiles on its own as C99 and C++11 with warnings as
+    errors, and a C caller can take the address of every declared function."""
+    compiler = "gcc" if lang == "c" else "g++"
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    funcs = declared_functions()
+    body = "\n".join(f"  p = (const void *)&{f}; (void)p;" for f in funcs)
+    src.write_text(f'#include "kda.h"\nint main(void) {{\n  const void *p;\n{body}\n  return 0;\n}}\n')
+    r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", f"-std={std}",
+                        "-I", os.path.join(ROOT, "include"), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
