@@ -22,7 +22,8 @@ KDA_ERR_UNSUPPORTED = -8
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER, encoding="utf-8") as fh:
+        text = fh.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(",
                                  text, flags=re.M)))

@@ -17,7 +17,8 @@ import pytest
 import oracle
 import test_oracle_pins as pins
 
-SRC = open(os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")).read()
+with open(os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c"), encoding="utf-8") as _fh:
+    SRC = _fh.read()
 
 DECAY = "    /* decay first: S <- Diag(alpha_t) S */\n"
 UBLK = "    /* u = beta (v - S^T k), against the decayed state */\n"
