@@ -65,3 +65,31 @@ def test_segment_pairs_applied_in_order_give_the_serial_state(seed, T, d, n_cuts
     for a, b in zip(cuts[:-1], cuts[1:]):
         S = brute.apply_pair(brute.segment_pair(k[a:b], v[a:b], g[a:b], beta[a:b]), S)
     assert _rel(S, S_serial[0, 0]) < 1e-10
+
+
+@SETTINGS
+@given(seed=st.integers(0, 2**31 - 1), d=st.sampled_from([8, 16]),
+       lengths=st.lists(st.integers(0, 40), min_size=1, max_size=6))
+def test_packed_documents_are_independent_runs(seed, d, lengths):
+    """cu_seqlens packing: each document runs from its own initial state, as if
+    alone; an empty document passes its initial state through (systems page,
+    on document boundaries)."""
+    T = sum(lengths)
+    if T == 0:
+        lengths = lengths + [1]
+        T = 1
+    q, k, v, g, beta, _ = _inputs(seed, T, d, 0.3)
+    rng = np.random.default_rng(seed + 1)
+    N = len(lengths)
+    S0 = rng.standard_normal((N, 1, d, d)) * 0.3
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    o, S = oracle.recurrent(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None], S0,
+                            cu_seqlens=cu)
+    for n in range(N):
+        a, b = cu[n], cu[n + 1]
+        if a == b:
+            assert np.array_equal(S[n], S0[n])
+            continue
+        on, Sn = oracle.recurrent(q[a:b, None], k[a:b, None], v[a:b, None], g[a:b, None],
+                                  beta[a:b, None], S0[n:n + 1])
+        assert np.array_equal(o[a:b], on) and np.array_equal(S[n], Sn[0])
