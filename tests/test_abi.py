@@ -9,6 +9,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import linear_attention_fwd_amd as kda
@@ -305,3 +306,39 @@ def test_header_is_plain_c(lang, std, tmp_path):
                         "-I", os.path.join(ROOT, "include"), str(src)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None)
+@given(lengths=st.lists(st.integers(0, 3000), min_size=1, max_size=20),
+       interval=st.sampled_from([64, 128, 192, 512, 1024]))
+def test_checkpoint_indices_are_unique_and_in_range(lib, lengths, interval):
+    """Every checkpoint the header documents, index
+    (floor(cu[d] / 64) + d + j * interval / 64 - 1) / (interval / 64) for
+    j * interval < length of d, lies below kda_checkpoint_count and no two
+    (document, j) share one."""
+    N, T = len(lengths), sum(lengths)
+    count = lib.kda_checkpoint_count(N, T, interval)
+    assert count >= 1
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    step = interval // 64
+    seen = set()
+    for d, L in enumerate(lengths):
+        j = 1
+        while j * interval < L:
+            idx = (cu[d] // 64 + d + j * step - 1) // step
+            assert 0 <= idx < count
+            assert idx not in seen
+            seen.add(idx)
+            j += 1
+
+
+@settings(max_examples=60, deadline=None)
+@given(N=st.integers(1, 5000), T=st.integers(0, 1 << 24), H=st.integers(1, 128))
+def test_workspace_size_formula(lib, N, T, H):
+    """One 62 KiB image per head and chunk slot (floor(T / 64) + N slots), then
+    4 bytes per document rounded up to 256; no 32-bit overflow."""
+    want = (T // 64 + N) * H * 63488 + (4 * N + 255) // 256 * 256
+    assert lib.kda_chunk_fwd_workspace_size(N, T, H, 128, 128) == want
