@@ -39,6 +39,9 @@
  *     argument validation and launch status only; kernels run asynchronously.
  *   * Every argument the host can check is checked before any HIP call;
  *     failures return a negative kda_status and enqueue nothing.
+ *   * Sizes: H <= 65535 heads and T < 2^31 tokens (the kernels address one
+ *     64-token chunk of one head with 32-bit offsets); larger values return
+ *     KDA_ERR_SHAPE.
  *   * Values the host cannot see (device-resident lengths) are clamped in the
  *     kernel and reported through an optional device error flag.
  *   * No C++ exception crosses this interface.  kda_last_error() returns a
@@ -206,7 +209,10 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
 /* ------------------------------------------------------------------------- */
 /* kda_segment_scan -- intra-device context parallelism for long prefill.
  *
- * Same operator and arguments as kda_chunk_fwd.  The packed sequence is cut into
+ * Same operator and arguments as kda_chunk_fwd, except that final_state and
+ * initial_state must not overlap (KDA_ERR_UNSUPPORTED): the segments of one
+ * document run concurrently, so a document's final state may be written
+ * while another segment still reads initial states.  The packed sequence is cut into
  * n_segments segments.  Following equation (17) of the systems page and its
  * derivation (section "公式 (17) 的推导"):
  *   A. each (segment, head) computes its affine pair (M, S~) from a zero state
@@ -255,18 +261,27 @@ int kda_default_segments(void);
  * back in place and o receives the bonus token's output.
  *
  *   state        [S_pool, H, 128, 128] fp32, read and written in place
- *   state_slots  [N] int32 slot of each sequence in the pool, or NULL (slot = n)
+ *   S_pool       number of states in the pool (>= 0; >= N when state_slots is NULL)
+ *   state_slots  [N] int32 slot of each sequence in the pool, or NULL (slot = n).
+ *                A slot outside [0, S_pool) is skipped: that sequence's state is
+ *                neither read nor written, its outputs are written as zeros and
+ *                err_flag gets KDA_DECODE_ERR_SLOT.
  *   cq, ck, cv, cz  [N, W, H, 128] dtype  cached projected draft inputs
  *   cbeta        [N, W, H] dtype
  *   accepted     [N] int32 device; values outside [0, W] are clamped and
- *                reported through err_flag
+ *                reported through err_flag (KDA_DECODE_ERR_ACCEPTED)
  *   nq, nk, nv, nz  [N, H, 128] dtype  bonus-token inputs;  nbeta [N, H]
  *   A_log        [H] fp32 or NULL;  g_min as for kda_chunk_fwd
  *   o            [N, H, 128] dtype (written)
- *   err_flag     int32 device pointer or NULL; set to 1 when a length was clamped
- *                (never cleared by the library)
- * Slots must be distinct across the N sequences of one call. */
-int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
+ *   err_flag     int32 device pointer or NULL; the bits below are OR'ed into it
+ *                atomically (it is never cleared by the library)
+ * Slots must be distinct across the N sequences of one call.
+ * Errors: KDA_ERR_SHAPE for S_pool < 0, S_pool < N without state_slots, or
+ * S_pool * H above INT32_MAX; the rest as listed at the top of this file. */
+#define KDA_DECODE_ERR_ACCEPTED 1 /* an accepted length outside [0, W] was clamped */
+#define KDA_DECODE_ERR_SLOT 2     /* a state slot outside [0, S_pool) was skipped */
+int kda_decode_step(float *state, int32_t S_pool, const int32_t *state_slots, const void *cq,
+                    const void *ck,
                     const void *cv, const void *cz, const void *cbeta,
                     const int32_t *accepted, int32_t W, const void *nq, const void *nk,
                     const void *nv, const void *nz, const void *nbeta, const float *A_log,
@@ -292,8 +307,9 @@ int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, co
  *   o_window     [N, W2, H, 128] dtype (written): output of each window draft
  * Errors as for kda_decode_step; KDA_ERR_NULL when W2 > 0 and a window pointer
  * is NULL. */
-int kda_decode_step_window(float *state, const int32_t *state_slots, const void *cq,
-                           const void *ck, const void *cv, const void *cz, const void *cbeta,
+int kda_decode_step_window(float *state, int32_t S_pool, const int32_t *state_slots,
+                           const void *cq, const void *ck, const void *cv, const void *cz,
+                           const void *cbeta,
                            const int32_t *accepted, int32_t W, const void *nq, const void *nk,
                            const void *nv, const void *nz, const void *nbeta, const void *wq,
                            const void *wk, const void *wv, const void *wz, const void *wbeta,

@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 KDA_RAW_INPUTS = 0x100  # OR'ed into dtype: q, k unnormalised and beta a logit
 KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
+KDA_DECODE_ERR_ACCEPTED, KDA_DECODE_ERR_SLOT = 1, 2  # bits of a decode step's err_flag
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
@@ -89,10 +90,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_segment_scan_workspace_size.restype = ctypes.c_size_t
     lib.kda_default_segments.argtypes = []
     lib.kda_default_segments.restype = ctypes.c_int
-    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
-                                    f32, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                    vp, f32, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = ctypes.c_int
-    lib.kda_decode_step_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+    lib.kda_decode_step_window.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                            vp, vp, vp, vp, vp, i32, vp, f32, vp, vp, vp, i32, i32,
                                            i32, i32, i32, vp]
     lib.kda_decode_step_window.restype = ctypes.c_int
@@ -376,30 +377,76 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     return o, final_state
 
 
+def _decode_common(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta, A_log,
+                   state_slots, err_flag):
+    """Validate the decode tensors (device, dtype, contiguity, shapes); returns
+    (N, H, d, W, S_pool)."""
+    torch = _torch()
+    _dev(state, "state", torch.float32)
+    if nq.dim() != 3:
+        raise ValueError("nq must be [N, H, 128]")
+    N, H, d = nq.shape
+    dt = nq.dtype
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, d, d):
+        raise ValueError(f"state must be [S_pool, {H}, {d}, {d}], got {tuple(state.shape)}")
+    S_pool = int(state.shape[0])
+    for name, t in (("nk", nk), ("nv", nv), ("nz", nz)):
+        _dev(t, name, dt)
+        if tuple(t.shape) != (N, H, d):
+            raise ValueError(f"{name} must be [{N}, {H}, {d}], got {tuple(t.shape)}")
+    _dev(nq, "nq", dt)
+    _dev(nbeta, "nbeta", dt)
+    if tuple(nbeta.shape) != (N, H):
+        raise ValueError(f"nbeta must be [{N}, {H}], got {tuple(nbeta.shape)}")
+    W = 0
+    if cq is not None:
+        if cq.dim() != 4:
+            raise ValueError("cq must be [N, W, H, 128]")
+        W = int(cq.shape[1])
+        for name, t in (("cq", cq), ("ck", ck), ("cv", cv), ("cz", cz)):
+            _dev(t, name, dt)
+            if t is None or tuple(t.shape) != (N, W, H, d):
+                raise ValueError(f"{name} must be [{N}, {W}, {H}, {d}]")
+        _dev(cbeta, "cbeta", dt)
+        if cbeta is None or tuple(cbeta.shape) != (N, W, H):
+            raise ValueError(f"cbeta must be [{N}, {W}, {H}]")
+    _dev(accepted, "accepted", torch.int32)
+    if accepted is None or tuple(accepted.shape) != (N,):
+        raise ValueError(f"accepted must be [{N}] int32")
+    _dev(state_slots, "state_slots", torch.int32)
+    if state_slots is not None and tuple(state_slots.shape) != (N,):
+        raise ValueError(f"state_slots must be [{N}] int32")
+    if state_slots is None and S_pool < N:
+        raise ValueError(f"state holds {S_pool} states but there are {N} sequences "
+                         "(pass state_slots to map sequences into the pool)")
+    _dev(A_log, "A_log", torch.float32)
+    if A_log is not None and tuple(A_log.shape) != (H,):
+        raise ValueError(f"A_log must be [{H}] float32")
+    _dev(err_flag, "err_flag", torch.int32)
+    if err_flag is not None and err_flag.numel() < 1:
+        raise ValueError("err_flag must hold one int32")
+    return N, H, d, W, S_pool
+
+
 def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
                     A_log=None, g_min: float = -5.0, state_slots=None, o=None, err_flag=None,
                     raw_inputs: bool = False):
     """One decode step with speculative-verify replay, updating ``state`` in place.
 
     state: [S_pool, H, 128, 128] fp32; cq, ck, cv, cz: [N, W, H, 128]; cbeta: [N, W, H];
-    accepted: [N] int32 (device); nq, nk, nv, nz: [N, H, 128]; nbeta: [N, H].
-    Returns o [N, H, 128] (output of the bonus token)."""
+    accepted: [N] int32 (device); nq, nk, nv, nz: [N, H, 128]; nbeta: [N, H];
+    state_slots: [N] int32 slots into the pool (None: sequence n uses state n).
+    Slots outside the pool are skipped (outputs zero, err_flag bit
+    KDA_DECODE_ERR_SLOT).  Returns o [N, H, 128] (output of the bonus token)."""
     torch = _torch()
     lib = load_library()
-    _dev(state, "state", torch.float32)
-    N, H, d = nq.shape
-    W = cq.shape[1] if cq is not None else 0
+    N, H, d, W, S_pool = _decode_common(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz,
+                                        nbeta, A_log, state_slots, err_flag)
     dt = nq.dtype
-    for name, t in (("cq", cq), ("ck", ck), ("cv", cv), ("cz", cz), ("cbeta", cbeta), ("nq", nq),
-                    ("nk", nk), ("nv", nv), ("nz", nz), ("nbeta", nbeta)):
-        _dev(t, name, dt)
-    _dev(accepted, "accepted", torch.int32)
-    _dev(state_slots, "state_slots", torch.int32)
-    _dev(A_log, "A_log", torch.float32)
-    _dev(err_flag, "err_flag", torch.int32)
     if o is None:
         o = torch.empty((N, H, d), dtype=dt, device=nq.device)
-    rc = lib.kda_decode_step(_ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
+    _dev(o, "o", dt)
+    rc = lib.kda_decode_step(_ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
                              _ptr(cz), _ptr(cbeta), _ptr(accepted), int(W), _ptr(nq), _ptr(nk),
                              _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(A_log), float(g_min), _ptr(o),
                              _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())
@@ -419,31 +466,25 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
     o [N, H, 128] for the bonus token, o_window [N, W2, H, 128] for the drafts."""
     torch = _torch()
     lib = load_library()
-    _dev(state, "state", torch.float32)
-    N, H, d = nq.shape
-    W = cq.shape[1] if cq is not None else 0
+    N, H, d, W, S_pool = _decode_common(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz,
+                                        nbeta, A_log, state_slots, err_flag)
     W2 = wq.shape[1]
     dt = nq.dtype
-    for name, t in (("cq", cq), ("ck", ck), ("cv", cv), ("cz", cz), ("cbeta", cbeta), ("nq", nq),
-                    ("nk", nk), ("nv", nv), ("nz", nz), ("nbeta", nbeta), ("wq", wq), ("wk", wk),
-                    ("wv", wv), ("wz", wz), ("wbeta", wbeta)):
+    for name, t in (("wq", wq), ("wk", wk), ("wv", wv), ("wz", wz), ("wbeta", wbeta)):
         _dev(t, name, dt)
     for name, t in (("wk", wk), ("wv", wv), ("wz", wz)):
         if tuple(t.shape) != tuple(wq.shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(wq.shape)}")
     if tuple(wq.shape) != (N, W2, H, d) or tuple(wbeta.shape) != (N, W2, H):
         raise ValueError("next-window inputs must be [N, W2, H, 128] and [N, W2, H]")
-    _dev(accepted, "accepted", torch.int32)
-    _dev(state_slots, "state_slots", torch.int32)
-    _dev(A_log, "A_log", torch.float32)
-    _dev(err_flag, "err_flag", torch.int32)
     if o is None:
         o = torch.empty((N, H, d), dtype=dt, device=nq.device)
     if o_window is None:
         o_window = torch.empty((N, W2, H, d), dtype=dt, device=nq.device)
     _dev(o_window, "o_window", dt)
+    _dev(o, "o", dt)
     rc = lib.kda_decode_step_window(
-        _ptr(state), _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
+        _ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
         _ptr(accepted), int(W), _ptr(nq), _ptr(nk), _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(wq),
         _ptr(wk), _ptr(wv), _ptr(wz), _ptr(wbeta), int(W2), _ptr(A_log), float(g_min), _ptr(o),
         _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())

@@ -30,6 +30,10 @@ int hip_fail(hipError_t e, const char *what) {
 
 constexpr int kD = 128;
 constexpr int kC = 64;  // chunk length
+// The kernels address the rows of one 64-token chunk of one head with 32-bit
+// byte offsets: up to 64 tokens x H heads x 128 channels x 4 bytes.
+constexpr int kMaxHeads = 65535;
+static_assert((int64_t)kC * kMaxHeads * kD * 4 <= (int64_t)INT32_MAX, "chunk offsets fit int32");
 
 // The KDA_RAW_INPUTS flag of a dtype argument; the element type is the rest.
 bool take_raw_flag(int32_t &dtype) {
@@ -46,6 +50,7 @@ int check_layout(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int3
                  int32_t H, int32_t dk, int32_t dv, int32_t dtype) {
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported (got %d, %d)", dk, dv);
   if (H <= 0) return fail(KDA_ERR_SHAPE, "H must be positive (got %d)", H);
+  if (H > kMaxHeads) return fail(KDA_ERR_SHAPE, "H must be at most %d (got %d)", kMaxHeads, H);
   if (T < 0) return fail(KDA_ERR_SHAPE, "T must be >= 0");
   if (N <= 0) return fail(KDA_ERR_SHAPE, "N must be >= 1 (got %d)", N);
   if (T > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "T must fit int32 offsets");
@@ -430,8 +435,13 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
                          dk, dv, dtype, compute, o);
   if (rc != KDA_OK) return rc;
-  if (final_state && initial_state && final_state == initial_state)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not alias initial_state");
+  if (final_state && initial_state) {
+    // [N, H, D, D] fp32 each; any overlap is refused
+    const uintptr_t bytes = (uintptr_t)N * H * kD * kD * sizeof(float);
+    const uintptr_t f = (uintptr_t)final_state, i = (uintptr_t)initial_state;
+    if (f < i + bytes && i < f + bytes)
+      return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not overlap initial_state");
+  }
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   if (raw && f32c) return raw_unsupported("kda_segment_scan");
   int64_t req = n_segments;
@@ -547,7 +557,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   return KDA_OK;
 }
 
-static int decode_common(float *state, const int32_t *state_slots, const void *cq,
+static int decode_common(float *state, int32_t S_pool, const int32_t *state_slots, const void *cq,
                          const void *ck, const void *cv, const void *cz, const void *cbeta,
                          const int32_t *accepted, int32_t W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
@@ -558,10 +568,15 @@ static int decode_common(float *state, const int32_t *state_slots, const void *c
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
   if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
     return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");
+  if (H > kMaxHeads) return fail(KDA_ERR_SHAPE, "H must be at most %d (got %d)", kMaxHeads, H);
   if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "N * H too large");
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (!(g_min >= -5.0f && g_min < 0.0f))
     return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
+  if (S_pool < 0) return fail(KDA_ERR_SHAPE, "S_pool must be >= 0 (got %d)", S_pool);
+  if (!state_slots && S_pool < N)
+    return fail(KDA_ERR_SHAPE, "without state_slots the pool needs N = %d states (S_pool = %d)", N, S_pool);
+  if ((int64_t)S_pool * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "S_pool * H too large");
   if (N == 0) return KDA_OK;
   if (!state || !accepted || !nq || !nk || !nv || !nz || !nbeta || !o)
     return fail(KDA_ERR_NULL, "state, accepted, bonus inputs and o must be non-NULL");
@@ -573,26 +588,29 @@ static int decode_common(float *state, const int32_t *state_slots, const void *c
   hipError_t e = (dtype == KDA_BF16)
       ? kda::launch_decode<kda::bf16_t>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq,
                                         nk, nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N,
-                                        H, st)
+                                        H, S_pool, st)
       : kda::launch_decode<float>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk,
-                                  nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N, H, st);
+                                  nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N, H,
+                                  S_pool, st);
   if (e != hipSuccess) return hip_fail(e, who);
   return KDA_OK;
 }
 
-int kda_decode_step(float *state, const int32_t *state_slots, const void *cq, const void *ck,
+int kda_decode_step(float *state, int32_t S_pool, const int32_t *state_slots, const void *cq,
+                    const void *ck,
                     const void *cv, const void *cz, const void *cbeta,
                     const int32_t *accepted, int32_t W, const void *nq, const void *nk,
                     const void *nv, const void *nz, const void *nbeta, const float *A_log,
                     float g_min, void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
                     int32_t dv, int32_t dtype, void *stream) {
   const kda::DecodeWindowArgs none{0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  return decode_common(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv, nz,
-                       nbeta, none, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
+  return decode_common(state, S_pool, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv,
+                       nz, nbeta, none, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
                        "kda_decode_step launch");
 }
 
-int kda_decode_step_window(float *state, const int32_t *state_slots, const void *cq,
+int kda_decode_step_window(float *state, int32_t S_pool, const int32_t *state_slots,
+                           const void *cq,
                            const void *ck, const void *cv, const void *cz, const void *cbeta,
                            const int32_t *accepted, int32_t W, const void *nq, const void *nk,
                            const void *nv, const void *nz, const void *nbeta, const void *wq,
@@ -601,8 +619,8 @@ int kda_decode_step_window(float *state, const int32_t *state_slots, const void 
                            int32_t *err_flag, int32_t N, int32_t H, int32_t dk, int32_t dv,
                            int32_t dtype, void *stream) {
   const kda::DecodeWindowArgs win{W2, wq, wk, wv, wz, wbeta, o_window};
-  return decode_common(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv, nz,
-                       nbeta, win, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
+  return decode_common(state, S_pool, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk, nv,
+                       nz, nbeta, win, A_log, g_min, o, err_flag, N, H, dk, dv, dtype, stream,
                        "kda_decode_step_window launch");
 }
 

@@ -33,6 +33,9 @@ template <typename Tin> struct DecodeWindow {
   Tin *o;
 };
 constexpr int DEC_TOKBATCH = 8;  // tokens staged in LDS at a time
+// bits of the error flag
+constexpr int DEC_ERR_ACCEPTED = 1;  // an accepted length outside [0, W] was clamped
+constexpr int DEC_ERR_SLOT = 2;      // a state slot outside [0, S_pool) was skipped
 
 
 // RAW: q, k unnormalised and beta a logit (normalised and sigmoid applied here)
@@ -46,7 +49,7 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                   const Tin *__restrict__ nv, const Tin *__restrict__ nz,
                   const Tin *__restrict__ nbeta, DecodeWindow<Tin> win,
                   const float *__restrict__ A_log, float g_min, Tin *__restrict__ o,
-                  int32_t *__restrict__ err_flag, int H) {
+                  int32_t *__restrict__ err_flag, int H, int S_pool) {
   __shared__ __align__(16) float s_k[DEC_TOKBATCH][D];
   __shared__ float s_qsc[DEC_TOKBATCH], s_ksc[DEC_TOKBATCH];  // raw inputs: 1 / ||q||, 1 / ||k||
   __shared__ __align__(16) float s_q[DEC_TOKBATCH][D];
@@ -64,15 +67,29 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
   const int col0 = wave * 32 + cg * 4;
   const int row0 = rg * 16;
 
+  // A slot outside the pool [0, S_pool) touches no state: the sequence's
+  // outputs are written as zeros and DEC_ERR_SLOT is set in the error flag.
+  const int64_t slot = slots ? (int64_t)slots[n] : (int64_t)n;
+  if (slot < 0 || slot >= S_pool) {
+    if (tid == 0 && err_flag)
+      __hip_atomic_fetch_or(err_flag, DEC_ERR_SLOT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int x = tid; x < (1 + win.W2) * D; x += DEC_THREADS) {
+      const int t = x / D, c = x % D;
+      Tin *dst = t == 0 ? o + ((int64_t)n * H + h) * D
+                        : win.o + (((int64_t)n * win.W2 + (t - 1)) * H + h) * D;
+      io<Tin>::store1(dst + c, 0.f);
+    }
+    return;
+  }
   int acc = accepted[n];
   if (acc < 0 || acc > W) {
-    if (tid == 0 && err_flag) *err_flag = 1;
+    if (tid == 0 && err_flag)
+      __hip_atomic_fetch_or(err_flag, DEC_ERR_ACCEPTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     acc = acc < 0 ? 0 : W;
   }
   // tokens: the acc accepted drafts (replayed), the bonus token, then the
   // W2 drafts of the next window (outputs only; their states are not kept)
   const int ntok = acc + 1 + win.W2;
-  const int64_t slot = slots ? (int64_t)slots[n] : (int64_t)n;
   float *__restrict__ Sg = state + (slot * H + h) * (int64_t)(D * D);
 
   // Stream the state slice into registers: 16 rows x 4 columns per lane.  The
@@ -237,7 +254,8 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const int32_t *accepted, int W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
                          const DecodeWindowArgs &w, bool raw, const float *A_log, float g_min,
-                         void *o, int32_t *err_flag, int N, int H, hipStream_t stream) {
+                         void *o, int32_t *err_flag, int N, int H, int S_pool,
+                         hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)N * H));
   DecodeWindow<Tin> win{w.W2, (const Tin *)w.q, (const Tin *)w.k, (const Tin *)w.v,
                         (const Tin *)w.z, (const Tin *)w.beta, (Tin *)w.o};
@@ -245,7 +263,8 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
   hipLaunchKernelGGL(kernel, grid, dim3(DEC_THREADS), 0, stream, state, slots, (const Tin *)cq,
                      (const Tin *)ck, (const Tin *)cv, (const Tin *)cz, (const Tin *)cbeta,
                      accepted, W, (const Tin *)nq, (const Tin *)nk, (const Tin *)nv,
-                     (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min, (Tin *)o, err_flag, H);
+                     (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min, (Tin *)o, err_flag, H,
+                     S_pool);
   return hipGetLastError();
 }
 
@@ -254,12 +273,12 @@ template hipError_t launch_decode<float>(float *, const int32_t *, const void *,
                                          const int32_t *, int, const void *, const void *,
                                          const void *, const void *, const void *,
                                          const DecodeWindowArgs &, bool, const float *, float,
-                                         void *, int32_t *, int, int, hipStream_t);
+                                         void *, int32_t *, int, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(float *, const int32_t *, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const int32_t *, int, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const DecodeWindowArgs &, bool, const float *, float,
-                                          void *, int32_t *, int, int, hipStream_t);
+                                          void *, int32_t *, int, int, int, hipStream_t);
 
 }  // namespace kda

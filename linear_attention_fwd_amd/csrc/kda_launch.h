@@ -80,10 +80,17 @@ struct SplitParams {
   int32_t *order;
 };
 constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
+// Bytes of one chunk image (the recurrence operands of one (head, chunk);
+// the layout is ChunkImage in kda_split.hip, which checks this size).
+constexpr int64_t CHUNK_IMAGE_BYTES = 63488;
 // chunk images [H, n_slots, image], then the document order (4 N bytes,
 // rounded up to 256)
-size_t split_workspace_bytes(int64_t T, int N, int H);
-size_t split_order_offset(int64_t T, int N, int H);
+inline size_t split_order_offset(int64_t T, int N, int H) {
+  return (size_t)n_chunk_slots(T, N) * (size_t)H * (size_t)CHUNK_IMAGE_BYTES;
+}
+inline size_t split_workspace_bytes(int64_t T, int N, int H) {
+  return split_order_offset(T, N, H) + ((size_t)N * 4 + 255) / 256 * 256;
+}
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);
 
@@ -128,6 +135,6 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const void *nv, const void *nz, const void *nbeta,
                          const DecodeWindowArgs &win, bool raw, const float *A_log,
                          float g_min, void *o, int32_t *err_flag, int N, int H,
-                         hipStream_t stream);
+                         int S_pool, hipStream_t stream);
 
 }  // namespace kda

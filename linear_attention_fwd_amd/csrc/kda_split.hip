@@ -49,6 +49,7 @@ struct __align__(16) ChunkImage {
 constexpr int IMG_BYTES = (int)sizeof(ChunkImage);
 constexpr int IMG_BLOCKS = IMG_BYTES / 1024;
 static_assert(IMG_BYTES % 1024 == 0, "chunk image must be whole 1 KB blocks");
+static_assert(IMG_BYTES == CHUNK_IMAGE_BYTES, "workspace formula of kda_launch.h");
 static_assert(offsetof(ChunkImage, Qd) % 1024 == 0 && offsetof(ChunkImage, KrT) % 1024 == 0 &&
                   offsetof(ChunkImage, Mqk) % 1024 == 0 && offsetof(ChunkImage, INVb) % 1024 == 0,
               "operand tiles must start on copy-block boundaries");
@@ -752,13 +753,6 @@ __global__ void __launch_bounds__(ORDER_THREADS) kda_doc_order_kernel(const int3
     base[t] += add;
     __syncthreads();
   }
-}
-
-size_t split_order_offset(int64_t T, int N, int H) {
-  return (size_t)n_chunk_slots(T, N) * (size_t)H * (size_t)IMG_BYTES;
-}
-size_t split_workspace_bytes(int64_t T, int N, int H) {
-  return split_order_offset(T, N, H) + ((size_t)N * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream) {

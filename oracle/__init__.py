@@ -49,9 +49,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    # KDA_ORACLE_LIB: another build of kda_oracle.c (the tests run the pins on a
+    # sanitizer build this way)
+    path = os.environ.get("KDA_ORACLE_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.kda_oracle_gate.argtypes = [dp, dp, ctypes.c_double, ctypes.c_int64, ctypes.c_int32,

@@ -44,6 +44,38 @@ def rel_l2_slices(x, ref, cu=None, axis_tokens=True):
     return worst, glob
 
 
+# Per-token bound on outputs: for every (document, head) slice and every token t
+# of it, ||o_t - o_ref_t||_2 / rms_t'(||o_ref_t'||_2) (the token's error against
+# the slice's root-mean-square token norm).  The slice tolerance above bounds the
+# average of these; this bounds the worst single token, so one wrong token or a
+# bad partial chunk cannot hide in a long slice.  bf16-MFMA arithmetic: 5e-2
+# (five times the slice tolerance); fp32 arithmetic: 1e-3.
+TOK_BF16 = 5e-2
+TOK_F32 = 1e-3
+
+
+def token_err_max(x, ref, cu=None, head_block=8):
+    """Max over (document, head, token) of ||x_t - ref_t|| / rms of ||ref_t|| over
+    the document's tokens of that head; outputs [T, H, D].  Documents whose
+    reference is all zero are skipped."""
+    T, H = ref.shape[:2]
+    bounds = [(0, T)] if cu is None else [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])]
+    worst = 0.0
+    for h0 in range(0, H, head_block):
+        xs = np.asarray(x[:, h0:h0 + head_block], dtype=np.float64)
+        rs = np.asarray(ref[:, h0:h0 + head_block], dtype=np.float64)
+        en = np.sqrt(np.sum((xs - rs) ** 2, axis=-1))     # [T, hb]
+        rn2 = np.sum(rs * rs, axis=-1)                      # [T, hb]
+        for a, b in bounds:
+            if b <= a:
+                continue
+            rms = np.sqrt(np.mean(rn2[a:b], axis=0))        # [hb]
+            ok = rms > 0
+            if np.any(ok):
+                worst = max(worst, float(np.max(en[a:b][:, ok] / rms[ok])))
+    return worst
+
+
 def _slice_f32(t, hs):
     """fp32 values of heads hs of a kda_gen.Tensor [T, H, ...], converting only the slice."""
     x = t.data[:, hs]

@@ -204,14 +204,22 @@ def test_checkpoint_validation(lib):
 
 def test_decode_validation(lib):
     def call(**kw):
-        a = dict(state=FAKE, slots=None, c=FAKE, acc=FAKE, W=4, n=FAKE, A=None, g_min=-5.0,
-                 o=FAKE, err=None, N=8, H=4, dk=128, dv=128, dtype=1)
+        a = dict(state=FAKE, pool=8, slots=None, c=FAKE, acc=FAKE, W=4, n=FAKE, A=None,
+                 g_min=-5.0, o=FAKE, err=None, N=8, H=4, dk=128, dv=128, dtype=1)
         a.update(kw)
         c, n = a["c"], a["n"]
-        return lib.kda_decode_step(a["state"], a["slots"], c, c, c, c, c, a["acc"], a["W"], n, n,
-                                   n, n, n, a["A"], a["g_min"], a["o"], a["err"], a["N"], a["H"],
-                                   a["dk"], a["dv"], a["dtype"], None)
+        return lib.kda_decode_step(a["state"], a["pool"], a["slots"], c, c, c, c, c, a["acc"],
+                                   a["W"], n, n, n, n, n, a["A"], a["g_min"], a["o"], a["err"],
+                                   a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
     assert call(state=None) == KDA_ERR_NULL
+    # the pool: without slots every sequence needs its own state; with slots the
+    # kernel skips any slot outside [0, S_pool) (checked there, not here)
+    assert call(pool=7) == KDA_ERR_SHAPE
+    assert call(pool=-1) == KDA_ERR_SHAPE
+    assert call(pool=-1, slots=FAKE) == KDA_ERR_SHAPE
+    assert call(pool=1, slots=FAKE, state=None) == KDA_ERR_NULL  # a small pool is fine with slots
+    assert call(pool=(1 << 31) - 1, H=4, state=None) == KDA_ERR_SHAPE  # S_pool * H overflows
+    assert call(H=65536) == KDA_ERR_SHAPE
     assert call(acc=None) == KDA_ERR_NULL
     assert call(n=None) == KDA_ERR_NULL
     assert call(c=None) == KDA_ERR_NULL          # drafts needed when W > 0
@@ -241,8 +249,8 @@ def test_raw_inputs_flag(lib):
                                     256, 4, 128, 128, 1 | RAW, 1, n_seg, FAKE, None, FAKE, 1 << 30,
                                     None) == KDA_ERR_UNSUPPORTED
     # accepted by decode (rejected here only for the missing state)
-    assert lib.kda_decode_step(None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE,
-                               FAKE, FAKE, None, -5.0, FAKE, None, 8, 4, 128, 128, 1 | RAW,
+    assert lib.kda_decode_step(None, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, None, -5.0, FAKE, None, 8, 4, 128, 128, 1 | RAW,
                                None) == KDA_ERR_NULL
 
 
@@ -263,11 +271,12 @@ def test_unbounded_validation(lib):
 
 def test_decode_window_validation(lib):
     def call(**kw):
-        a = dict(state=FAKE, c=FAKE, acc=FAKE, W=4, n=FAKE, w=FAKE, W2=4, o=FAKE, ow=FAKE,
+        a = dict(state=FAKE, pool=8, c=FAKE, acc=FAKE, W=4, n=FAKE, w=FAKE, W2=4, o=FAKE, ow=FAKE,
                  N=8, H=4, dtype=1)
         a.update(kw)
         c, n, w = a["c"], a["n"], a["w"]
-        return lib.kda_decode_step_window(a["state"], None, c, c, c, c, c, a["acc"], a["W"], n, n,
+        return lib.kda_decode_step_window(a["state"], a["pool"], None, c, c, c, c, c, a["acc"],
+                                          a["W"], n, n,
                                           n, n, n, w, w, w, w, w, a["W2"], None, -5.0, a["o"],
                                           a["ow"], None, a["N"], a["H"], 128, 128, a["dtype"],
                                           None)
@@ -276,7 +285,49 @@ def test_decode_window_validation(lib):
     assert call(W2=-1) == KDA_ERR_SHAPE
     assert call(dtype=5) == KDA_ERR_DTYPE
     assert call(state=None) == KDA_ERR_NULL
+    assert call(pool=4) == KDA_ERR_SHAPE
     assert call(N=0) == KDA_OK
+
+
+def test_segment_scan_refuses_overlapping_states(lib):
+    """kda_segment_scan runs the segments of a document concurrently, so its
+    final states must not overlap the initial states: exact aliasing and partial
+    overlaps in either direction are refused before anything is launched, and
+    adjacent ranges are accepted (then refused for the missing workspace)."""
+    N, H = 3, 4
+    nbytes = N * H * 128 * 128 * 4
+    base = 1 << 32
+
+    def call(init, fin, ws=None):
+        return lib.kda_segment_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, ctypes.c_void_p(init),
+                                    FAKE, np.array([0, 64, 128, 256], np.int32).ctypes.data_as(
+                                        ctypes.c_void_p), N, 256, H, 128, 128, 1, 0, 7, FAKE,
+                                    ctypes.c_void_p(fin), ws, 0, None)
+    assert call(base, base) == KDA_ERR_UNSUPPORTED
+    assert call(base, base + 4096) == KDA_ERR_UNSUPPORTED
+    assert call(base + nbytes - 4, base) == KDA_ERR_UNSUPPORTED
+    assert call(base, base + nbytes - 4) == KDA_ERR_UNSUPPORTED
+    assert call(base, base + nbytes) == KDA_ERR_WORKSPACE     # adjacent: no overlap
+    assert call(base + nbytes, base) == KDA_ERR_WORKSPACE
+
+
+def test_head_count_bound(lib):
+    """H above 65535 would overflow the kernels' 32-bit chunk offsets (64 tokens
+    x H x 128 channels x 4 bytes): refused by every prefill entry point."""
+    big = 65536
+    ok = 65535
+    assert lib.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1, 256,
+                             big, 128, 128, 1, 0, FAKE, None, None, 0, None) == KDA_ERR_SHAPE
+    assert lib.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1, 256,
+                             ok, 128, 128, 1, 0, FAKE, None, FAKE, 0, None) == KDA_ERR_WORKSPACE
+    assert lib.kda_chunk_prep(FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, 1, 256, big, 128,
+                              128, 1, FAKE, 1 << 40, None) == KDA_ERR_SHAPE
+    assert lib.kda_segment_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1, 256,
+                                big, 128, 128, 1, 0, 7, FAKE, None, FAKE, 1 << 40,
+                                None) == KDA_ERR_SHAPE
+    assert lib.kda_chunk_fwd_unbounded(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 1, 256,
+                                       big, 128, 128, 1, FAKE, None, FAKE, 1 << 40,
+                                       None) == KDA_ERR_SHAPE
 
 
 def test_one_hip_runtime_per_process():

@@ -557,6 +557,45 @@ def test_decode_slots_and_clamping():
     assert np.all(P[untouched] == 0)
 
 
+@pytest.mark.parametrize("W2", [0, 3])
+def test_decode_skips_slots_outside_the_pool(W2):
+    """Slots -1 and S_pool (a padding convention and an off-by-one) are skipped:
+    the pool is neither read nor written there, those sequences' outputs are
+    zeros, err_flag gets the slot bit, and every other sequence is unaffected."""
+    import torch
+    import linear_attention_fwd_amd as kda
+    inp = kda_gen.make_decode(56, N=6, H=2, W=4, dtype="bf16", accepted=[1, 4, 0, 3, 2, 4], W2=W2)
+    S_pool = 8
+    slots = np.array([5, -1, 0, S_pool, 7, 2], dtype=np.int32)
+    good = slots >= 0
+    pool = np.full((S_pool, inp.H, 128, 128), 3.0, np.float32)  # sentinel for unused slots
+    pool[slots[good & (slots < S_pool)]] = inp.state[good & (slots < S_pool)]
+    print(f"[case] decode with slots {slots.tolist()} in a pool of {S_pool}, W2={W2}", flush=True)
+    t = decode_gpu_inputs(inp)
+    t["state"] = torch.from_numpy(pool).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sl = torch.from_numpy(slots).cuda()
+    if W2:
+        o, ow, P = gpu_decode_window(inp, t=t, state_slots=sl, err_flag=err)
+        _, ow_ref, _ = oracle.decode_window(inp)
+    else:
+        o, P = gpu_decode(inp, t=t, state_slots=sl, err_flag=err)
+    assert int(err.item()) == kda.KDA_DECODE_ERR_SLOT
+    bad = ~((slots >= 0) & (slots < S_pool))
+    assert np.all(o[bad] == 0)
+    o_ref, S_ref = oracle.decode(inp)
+    ok = ~bad
+    assert rel_l2_slices(P[slots[ok]], S_ref[ok], axis_tokens=False)[0] <= TOL_F32
+    assert rel_l2_slices(o[ok][:, :, None], o_ref[ok][:, :, None], axis_tokens=False)[0] <= TOL_BF16
+    if W2:
+        assert np.all(ow[bad] == 0)
+        assert rel_l2_slices(ow[ok].reshape(-1, inp.H, 128)[:, :, None],
+                             ow_ref[ok].reshape(-1, inp.H, 128)[:, :, None],
+                             axis_tokens=False)[0] <= TOL_BF16
+    untouched = np.setdiff1d(np.arange(S_pool), slots[ok])
+    assert np.all(P[untouched] == 3.0)
+
+
 @pytest.mark.parametrize("dtype,W2", [("bf16", 4), ("f32", 4), ("bf16", 13)])
 def test_decode_window_matches_oracle(dtype, W2):
     """Replay + bonus + next draft window in one kernel: the bonus output and the
