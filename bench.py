@@ -135,6 +135,11 @@ def measured_traffic(here: str, kernel: str):
     return None
 
 
+def _progress(msg: str) -> None:
+    """One progress line on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as fh:
@@ -325,6 +330,7 @@ def main():
 
     step_ms, step_mean, step_wall = timer.run(fwd, args.steps, args.warmup)
     tokens_per_s = T / (step_ms * 1e-3)
+    _progress(f"prefill step {step_ms:.4f} ms (median), {tokens_per_s / 1e6:.2f} M tokens/s")
 
     # the two kernels of the step, timed apart (same calls, an event between)
     prep_ms, rec_ms = timer.split(
@@ -381,6 +387,7 @@ def main():
                             o=d_o, raw_inputs=raw)
 
     dec_ms, _, _ = timer.run(dstep, args.decode_steps, args.warmup)
+    _progress(f"decode step {dec_ms:.4f} ms")
     dec_bytes = decode_state_bytes(dec.N, dec.H)
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     win_ms, _, _ = timer.run(lambda: kda.kda_decode_step_window(
@@ -401,12 +408,16 @@ def main():
     # ---------------- context lines: long prefill and packed varlen ----------
     context = {}
     for name, th in zip(wanted, threads):
-        th.join()
+        while th.is_alive():
+            th.join(timeout=30)
+            if th.is_alive():
+                _progress(f"still drawing the {name} inputs on the host")
         w = later.get(name)
         if isinstance(w, Exception) or w is None:
             context[name] = {"error": repr(w)}
             continue
         context[name] = context_line(name, w, np, torch, kda_gen, kda, dev, timer, args)
+        _progress(f"{name} prefill {context[name]['ms_per_step']:.4f} ms")
         later.pop(name, None)
 
     # ---------------- CPU oracle baseline (this machine's host cores; after the
