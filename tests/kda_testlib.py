@@ -45,19 +45,22 @@ def rel_l2_slices(x, ref, cu=None, axis_tokens=True):
 
 
 # Per-token bound on outputs: for every (document, head) slice and every token t
-# of it, ||o_t - o_ref_t||_2 / rms_t'(||o_ref_t'||_2) (the token's error against
-# the slice's root-mean-square token norm).  The slice tolerance above bounds the
-# average of these; this bounds the worst single token, so one wrong token or a
-# bad partial chunk cannot hide in a long slice.  bf16-MFMA arithmetic: 5e-2
-# (five times the slice tolerance); fp32 arithmetic: 1e-3.
+# of it, ||o_t - o_ref_t||_2 / max(||o_ref_t||_2, rms_t'(||o_ref_t'||_2)), the
+# token's error against the larger of its own norm and the slice's
+# root-mean-square token norm (the floor keeps near-zero outputs from dividing
+# by almost nothing).  The slice tolerance above bounds an average of these;
+# this bounds the worst single token, so one wrong token or a bad partial chunk
+# cannot hide in a long slice.  bf16-MFMA arithmetic: 5e-2 (five times the
+# slice tolerance); fp32 arithmetic: 1e-3, plus 2^-8 when O is stored in bf16
+# (rounding a vector to bf16 moves it by at most 2^-8 of its own norm).
 TOK_BF16 = 5e-2
 TOK_F32 = 1e-3
 
 
 def token_err_max(x, ref, cu=None, head_block=8):
-    """Max over (document, head, token) of ||x_t - ref_t|| / rms of ||ref_t|| over
-    the document's tokens of that head; outputs [T, H, D].  Documents whose
-    reference is all zero are skipped."""
+    """Max over (document, head, token) of ||x_t - ref_t|| / max(||ref_t||, rms of
+    ||ref_t'|| over the document's tokens of that head); outputs [T, H, D].
+    Documents whose reference is all zero are skipped."""
     T, H = ref.shape[:2]
     bounds = [(0, T)] if cu is None else [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])]
     worst = 0.0
@@ -72,7 +75,8 @@ def token_err_max(x, ref, cu=None, head_block=8):
             rms = np.sqrt(np.mean(rn2[a:b], axis=0))        # [hb]
             ok = rms > 0
             if np.any(ok):
-                worst = max(worst, float(np.max(en[a:b][:, ok] / rms[ok])))
+                den = np.maximum(np.sqrt(rn2[a:b][:, ok]), rms[ok])
+                worst = max(worst, float(np.max(en[a:b][:, ok] / den)))
     return worst
 
 
