@@ -129,6 +129,29 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
  * first; the order does not change any result).  0 for invalid sizes. */
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv);
 
+/* kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same two-kernel prefill, with its workspace in a
+ * static device array of KDA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends.  Nothing is allocated
+ * by the call; the caller still passes the inputs and outputs.
+ *
+ * Arguments as for kda_chunk_fwd without compute and the workspace: bf16 inputs
+ * (KDA_RAW_INPUTS allowed), bf16 arithmetic.  Sizes whose workspace,
+ * kda_chunk_fwd_workspace_size(N, T, H, 128, 128), exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE (e.g. T = 8192 at H = 32,
+ * or T = 65536 at H = 4, fit; T = 8192 at H = 96 does not).  The scratch keeps
+ * the last call's contents and needs no clearing (every call writes what it
+ * reads).  Calls that overlap on one GPU (different streams, or host threads)
+ * share the scratch and race: order them on one stream. */
+#define KDA_NOALLOC_SCRATCH_BYTES 268435456
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_logits,
+                          const void *beta, const float *A_log, float g_min,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                          int32_t dk, int32_t dv, int32_t dtype, void *o, float *final_state,
+                          void *stream);
+
 /* The two halves of kda_chunk_fwd's two-kernel path, callable on their own
  * (bf16 inputs and arithmetic only; KDA_ERR_UNSUPPORTED otherwise).
  *

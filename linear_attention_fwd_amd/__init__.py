@@ -11,6 +11,7 @@ KDA_RAW_INPUTS in the C ABI).
 
 Entry points (same names as the C ABI):
   * ``kda_chunk_fwd``    -- chunkwise prefill of packed documents
+  * ``kda_chunk_fwd_noalloc`` -- the same with the library's static device scratch
   * ``kda_chunk_fwd_unbounded`` -- the same with the unbounded (softplus) gate
   * ``kda_segment_scan`` -- prefill with intra-device segment pairs + scan
   * ``kda_decode_step``  -- decode step with speculative-verify replay
@@ -34,7 +35,8 @@ KDA_DECODE_ERR_ACCEPTED, KDA_DECODE_ERR_SLOT = 1, 2  # bits of a decode step's e
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_GATE_BOUND", -5: "KDA_ERR_SEQLENS", -6: "KDA_ERR_WORKSPACE",
           -7: "KDA_ERR_HIP", -8: "KDA_ERR_UNSUPPORTED"}
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_unbounded", "kda_chunk_fwd_workspace_size",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_unbounded",
+           "kda_chunk_fwd_workspace_size",
            "kda_chunk_prep",
            "kda_chunk_recurrence", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count",
            "kda_segment_scan",
@@ -68,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     prefill = [vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32]
     lib.kda_chunk_fwd.argtypes = prefill + [vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = prefill[:-1] + [vp, vp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_unbounded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                             i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_unbounded.restype = ctypes.c_int
@@ -218,6 +222,35 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                            dk, dv, _dtype_code(q, raw_inputs), int(compute), _ptr(o),
                            _ptr(final_state),
                            ws_ptr, ws_bytes, _stream())
+    _check(rc)
+    return o, final_state
+
+
+KDA_NOALLOC_SCRATCH_BYTES = 256 << 20  # kda_chunk_fwd_noalloc's device scratch
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
+                          initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                          output_final_state: bool = True, o=None, final_state=None,
+                          raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
+    """``kda_chunk_fwd`` (two-kernel path, bf16) whose workspace is the library's
+    static device scratch: the C call allocates nothing.  Sizes whose workspace
+    exceeds KDA_NOALLOC_SCRATCH_BYTES raise KDAError (KDA_ERR_WORKSPACE).  Pass
+    ``o`` (and ``final_state``) to allocate nothing here either.
+    Returns (o, final_state) as ``kda_chunk_fwd``."""
+    torch = _torch()
+    lib = load_library()
+    T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
+                                                       initial_state, cu_seqlens, cu_seqlens_host)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
+                                   _ptr(A_log), float(g_min), _ptr(initial_state), _ptr(cu_dev),
+                                   host_ptr, N, T, H, dk, dv, _dtype_code(q, raw_inputs), _ptr(o),
+                                   _ptr(final_state), _stream())
     _check(rc)
     return o, final_state
 
@@ -492,7 +525,7 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
     return o, o_window
 
 
-__all__ = ["KDA_RAW_INPUTS", "kda_chunk_fwd", "kda_segment_scan", "kda_segment_scan_workspace_size",
+__all__ = ["KDA_RAW_INPUTS", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_segment_scan", "kda_segment_scan_workspace_size",
            "kda_default_segments", "kda_decode_step", "kda_decode_step_window",
            "kda_chunk_fwd_unbounded", "kda_chunk_fwd_checkpoints", "kda_checkpoint_count", "load_library", "KDAError",
            "KDA_COMPUTE_AUTO", "KDA_COMPUTE_F32"]

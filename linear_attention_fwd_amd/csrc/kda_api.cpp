@@ -270,6 +270,44 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
   return KDA_OK;
 }
 
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_logits,
+                          const void *beta, const float *A_log, float g_min,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H,
+                          int32_t dk, int32_t dv, int32_t dtype, void *o, float *final_state,
+                          void *stream) {
+  static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::NOALLOC_SCRATCH_BYTES, "documented limit");
+  const bool raw = take_raw_flag(dtype);
+  int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
+                         dk, dv, dtype, KDA_COMPUTE_AUTO, o);
+  if (rc != KDA_OK) return rc;
+  if (dtype != KDA_BF16)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd_noalloc runs the bf16 two-kernel path only");
+  const size_t need = kda::split_workspace_bytes(T, N, H);
+  if (need > kda::NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE,
+                "kda_chunk_fwd_noalloc: %zu bytes of scratch needed (N = %d, T = %lld, H = %d), "
+                "%zu available; call kda_chunk_fwd with a workspace instead",
+                need, N, (long long)T, H, kda::NOALLOC_SCRATCH_BYTES);
+  hipStream_t st = (hipStream_t)stream;
+  if (T > 0) {
+    void *ws = nullptr;
+    hipError_t e = kda::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc scratch address");
+    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
+                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state, ws);
+    p.raw = raw;
+    e = kda::launch_chunk_prep(p, st);
+    if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc launch");
+  }
+  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
+    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc empty documents");
+  }
+  return KDA_OK;
+}
+
 size_t kda_checkpoint_count(int32_t N, int64_t T, int32_t interval) {
   if (N <= 0 || T < 0 || interval <= 0 || interval % kC != 0) return 0;
   return (size_t)((kda::n_chunk_slots(T, N) - 1) / (interval / kC) + 1);

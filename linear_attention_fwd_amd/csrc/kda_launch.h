@@ -92,6 +92,10 @@ inline size_t split_workspace_bytes(int64_t T, int N, int H) {
   return split_order_offset(T, N, H) + ((size_t)N * 4 + 255) / 256 * 256;
 }
 hipError_t launch_chunk_prep(const SplitParams &p, hipStream_t stream);
+// Device scratch of kda_chunk_fwd_noalloc (kda_noalloc.hip): the address, on the
+// current device, of a static array of NOALLOC_SCRATCH_BYTES bytes.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)256 << 20;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream);
 
 // final_state[d] = initial_state[d] (or 0) for every empty document d;

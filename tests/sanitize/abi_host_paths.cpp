@@ -104,6 +104,17 @@ int main() {
            KDA_ERR_WORKSPACE);
   }
 
+  // ---- the no-allocation prefill: too large for its scratch, then a fit ----
+  EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, nullptr, nullptr, nullptr, 1, 8192, 96,
+                               128, 128, KDA_BF16, F, Ff, nullptr),
+         KDA_ERR_WORKSPACE);
+  EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, nullptr, nullptr, nullptr, 1, 8192, 4,
+                               128, 128, KDA_F32, F, Ff, nullptr),
+         KDA_ERR_UNSUPPORTED);
+  EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                               KDA_BF16, F, Ff, nullptr),
+         KDA_ERR_HIP);
+
   // ---- decode ----
   EXPECT(kda_decode_step(Ff, 7, nullptr, F, F, F, F, F, Fi, 4, F, F, F, F, F, Ff, -5.f, F,
                          nullptr, 8, H, 128, 128, KDA_BF16, nullptr),

@@ -38,6 +38,7 @@ hipError_t launch_pair_scan(const float *, const float *, const int32_t *, int, 
   return launched();
 }
 hipError_t launch_scan_chains(const ScanChains &, int, hipStream_t) { return launched(); }
+hipError_t noalloc_scratch(void **) { return launched(); }
 template <typename Tin>
 hipError_t launch_decode(float *, const int32_t *, const void *, const void *, const void *,
                          const void *, const void *, const int32_t *, int, const void *,
