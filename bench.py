@@ -94,6 +94,8 @@ def _parse():
     ap.add_argument("--workload", choices=["all", "prefill", "long", "varlen"], default="all",
                     help="all: the headline plus every context line; prefill: only the "
                          "single-sequence parts; long / varlen: only that line (profiling)")
+    ap.add_argument("--min-warm-s", type=float, default=MIN_WARM_S,
+                    help="shortest warm-up before each timed part, seconds (0 for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (used to "
                          "scale the HBM byte counters of a profiler) and exit")
@@ -155,13 +157,13 @@ class Timer:
     """HIP-event timing on the stream the library launches on (torch's current
     stream, whose handle the binding passes to every call)."""
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
+    def __init__(self, torch, stream, min_warm_s=MIN_WARM_S):
+        self.torch, self.stream, self.min_warm_s = torch, stream, min_warm_s
 
     def warm(self, fn, n):
         t0 = time.perf_counter()
         i = 0
-        while i < n or time.perf_counter() - t0 < MIN_WARM_S:
+        while i < n or time.perf_counter() - t0 < self.min_warm_s:
             fn()
             i += 1
             if i % 8 == 0:
@@ -305,7 +307,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    timer = Timer(torch, stream)
+    timer = Timer(torch, stream, args.min_warm_s)
 
     if args.workload in ("long", "varlen"):
         threads[0].join()

@@ -258,9 +258,10 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
 // workgroups of one unit share an XCD (blockIdx % 8), so the image reaches
 // them from one L2.
 // ---------------------------------------------------------------------------
-constexpr int REC_THREADS = 512;
 constexpr int REC_COMPUTE_WAVES = 4;
-constexpr int REC_COPY_THREADS = REC_THREADS - 64 * REC_COMPUTE_WAVES;
+constexpr int REC_COPY_WAVES = 4;
+constexpr int REC_THREADS = 64 * (REC_COMPUTE_WAVES + REC_COPY_WAVES);
+constexpr int REC_COPY_THREADS = 64 * REC_COPY_WAVES;
 template <int NT> struct __align__(16) RecSmem {
   static constexpr int SLICE = 64 * NT;  // state columns per workgroup
   ChunkImage buf[2];
@@ -276,36 +277,38 @@ __device__ __forceinline__ bf16x8 pack_tiles(floatx4 t0, floatx4 t1) {
   return to_bf16x8(floatx8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]});
 }
 
-// The chunk recurrence (chunk_recurrence in kda_chunk.h) for this wave's NT
-// tiles of 16 state columns, operands from the chunk image in LDS:
-//   U = INV Diag(beta) (V - K_decay S);  O = Q_decay S + M_qk U;
-//   S <- Diag(gamma^C) S + K_restore^T U.
-// Each phase reads its MFMA A-operand fragments in one batch (lane (g, j): row
-// 16m + j, k elements 32kb + 8g .. +7) and applies them to every tile.
-// with_o = false skips O (segment pairs, whose images are copied without
-// Q_decay and M_qk).  V: the v rows of the chunk in LDS (vld elements per row),
-// tile t of this wave at column vcol + 16 t.
-// O rows go through the bounded descriptor ro (tokens past the chunk are
-// dropped) at byte offset off_o + token * rowb + 32 t, off_o = (j * H * D +
-// first column of the lane) * 2.
-template <int NT>
-__device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][8], const bf16_t *V,
-                                         int vld, int vcol, bool with_o, __amdgpu_buffer_rsrc_t ro,
-                                         int off_o, int rowb, int g, int j) {
-  using TD = Tile<bf16_t, D>;
-  using TC = Tile<bf16_t, CH>;
-  using PL = PackedLower;
-  // fragments read per batch: the whole phase for one tile; one 16-row block
-  // at a time for two (each fragment then feeds twice the MFMA work, and the
-  // whole-phase batches would not fit the register budget)
-  constexpr int MB = NT == 1 ? 4 : 1;
+// Registers one chunk step carries from phase to phase: S packed to bf16 (the
+// B operand of the U' and O products), U, and U packed to bf16.
+template <int NT> struct RecRegs {
   bf16x8 sb[NT][4];
+  floatx4 U[NT][4];
+  bf16x8 ub[NT][2];
+};
+
+// The chunk recurrence (chunk_recurrence in kda_chunk.h) for this wave's NT
+// tiles of 16 state columns, operands from the chunk image in LDS, in four
+// phases that each read one part of the image:
+//   0: U' = V - K_decay S            (K_decay, V)
+//   1: U = INV Diag(beta) U'         (INV Diag(beta))
+//   2: O = Q_decay S + M_qk U        (Q_decay, M_qk)
+//   3: S <- Diag(gamma^C) S + K_restore^T U   (K_restore^T, gamma^C)
+// Each phase reads its MFMA A-operand fragments in one batch (lane (g, j): row
+// 16m + j, k elements 32kb + 8g .. +7) and applies them to every tile.  The
+// fragments read per batch are the whole phase for one tile, one 16-row block
+// at a time for two (each fragment then feeds twice the MFMA work, and the
+// whole-phase batches would not fit the register budget).
+// V: the v rows of the chunk in LDS (vld elements per row), tile t of this
+// wave at column vcol + 16 t.
+template <int NT>
+__device__ __forceinline__ void rec_phase0(const ChunkImage &im, const floatx4 (&S)[NT][8],
+                                           const bf16_t *V, int vld, int vcol, int g, int j,
+                                           RecRegs<NT> &R) {
+  using TD = Tile<bf16_t, D>;
+  constexpr int MB = NT == 1 ? 4 : 1;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sb[t][kb] = pack_tiles(S[t][2 * kb], S[t][2 * kb + 1]);
-  // U' = V - K_decay S
-  floatx4 U[NT][4];
+    for (int kb = 0; kb < 4; ++kb) R.sb[t][kb] = pack_tiles(S[t][2 * kb], S[t][2 * kb + 1]);
 #pragma unroll
   for (int m0 = 0; m0 < 4; m0 += MB) {
     bf16x8 kd[MB][4];
@@ -320,72 +323,87 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][
         const int m = m0 + mm;
         floatx4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(kd[mm][kb], sb[t][kb], x);
+        for (int kb = 0; kb < 4; ++kb) x = mfma_bf16_k32(kd[mm][kb], R.sb[t][kb], x);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          U[t][m][r] = bf16_to_f32(V[(16 * m + 4 * g + r) * vld + vcol + 16 * t + j]) - x[r];
+          R.U[t][m][r] = bf16_to_f32(V[(16 * m + 4 * g + r) * vld + vcol + 16 * t + j]) - x[r];
       }
   }
-  // U = INV Diag(beta) U'
-  {
-    bf16x8 inv[6];
-    int x = 0;
+}
+
+template <int NT>
+__device__ __forceinline__ void rec_phase1(const ChunkImage &im, int g, int j, RecRegs<NT> &R) {
+  using PL = PackedLower;
+  bf16x8 inv[6];
+  int x = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) inv[x] = frag(im.INVb, PL::idx(16 * m + j, 32 * kb + 8 * g));
+    for (int kb = 0; kb <= (m >> 1); ++kb, ++x) inv[x] = frag(im.INVb, PL::idx(16 * m + j, 32 * kb + 8 * g));
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      bf16x8 bb[2];
+  for (int t = 0; t < NT; ++t) {
+    bf16x8 bb[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(U[t][2 * kb], U[t][2 * kb + 1]);
-      x = 0;
+    for (int kb = 0; kb < 2; ++kb) bb[kb] = pack_tiles(R.U[t][2 * kb], R.U[t][2 * kb + 1]);
+    x = 0;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(inv[x], bb[kb], acc);
-        U[t][m] = acc;
-      }
+      for (int kb = 0; kb <= (m >> 1); ++kb, ++x) acc = mfma_bf16_k32(inv[x], bb[kb], acc);
+      R.U[t][m] = acc;
     }
   }
-  bf16x8 ub[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ub[t][kb] = pack_tiles(U[t][2 * kb], U[t][2 * kb + 1]);
-  // O = Q_decay S + M_qk U, formed transposed: with the operands of each
-  // product swapped, lane (g, j) ends up with token 16m + j, columns 4g..4g+3
-  // of the tile and stores them with one 8-byte write.  Its stores then
-  // complete while the state update runs.
-  if (with_o) {
+    for (int kb = 0; kb < 2; ++kb) R.ub[t][kb] = pack_tiles(R.U[t][2 * kb], R.U[t][2 * kb + 1]);
+}
+
+// O = Q_decay S + M_qk U, formed transposed: with the operands of each product
+// swapped, lane (g, j) ends up with token 16m + j, columns 4g..4g+3 of the
+// tile and stores them with one 8-byte write through the bounded descriptor
+// ro (tokens past the chunk are dropped) at byte offset off_o + token * rowb +
+// 32 t, off_o = (j * H * D + first column of the lane) * 2.  Its stores then
+// complete while the state update runs.
+template <int NT>
+__device__ __forceinline__ void rec_phase2(const ChunkImage &im, const RecRegs<NT> &R,
+                                           __amdgpu_buffer_rsrc_t ro, int off_o, int rowb, int g,
+                                           int j) {
+  using TD = Tile<bf16_t, D>;
+  using PL = PackedLower;
+  constexpr int MB = NT == 1 ? 4 : 1;
 #pragma unroll
-    for (int m0 = 0; m0 < 4; m0 += MB) {
-      bf16x8 qd[MB][4], mqk[MB][2];
+  for (int m0 = 0; m0 < 4; m0 += MB) {
+    bf16x8 qd[MB][4], mqk[MB][2];
 #pragma unroll
-      for (int mm = 0; mm < MB; ++mm) {
-        const int m = m0 + mm;
+    for (int mm = 0; mm < MB; ++mm) {
+      const int m = m0 + mm;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qd[mm][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
+      for (int kb = 0; kb < 4; ++kb) qd[mm][kb] = frag(im.Qd, TD::idx(16 * m + j, 32 * kb + 8 * g));
 #pragma unroll
-        for (int kb = 0; kb <= (m >> 1); ++kb) mqk[mm][kb] = frag(im.Mqk, PL::idx(16 * m + j, 32 * kb + 8 * g));
-      }
-#pragma unroll
-      for (int mm = 0; mm < MB; ++mm)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int m = m0 + mm;
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(sb[t][kb], qd[mm][kb], acc);
-#pragma unroll
-          for (int kb = 0; kb <= (m >> 1); ++kb) acc = mfma_bf16_k32(ub[t][kb], mqk[mm][kb], acc);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(acc)), ro,
-                                                off_o + (16 * m) * rowb + 32 * t, 0, 0);
-        }
+      for (int kb = 0; kb <= (m >> 1); ++kb) mqk[mm][kb] = frag(im.Mqk, PL::idx(16 * m + j, 32 * kb + 8 * g));
     }
+#pragma unroll
+    for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int m = m0 + mm;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = mfma_bf16_k32(R.sb[t][kb], qd[mm][kb], acc);
+#pragma unroll
+        for (int kb = 0; kb <= (m >> 1); ++kb) acc = mfma_bf16_k32(R.ub[t][kb], mqk[mm][kb], acc);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_bf16x4(acc)), ro,
+                                              off_o + (16 * m) * rowb + 32 * t, 0, 0);
+      }
   }
-  // S <- Diag(gamma^C) S + K_restore^T U
+}
+
+template <int NT>
+__device__ __forceinline__ void rec_phase3(const ChunkImage &im, floatx4 (&S)[NT][8],
+                                           const RecRegs<NT> &R, int g, int j) {
+  using TC = Tile<bf16_t, CH>;
   constexpr int MS = NT == 1 ? 8 : 2;
 #pragma unroll
   for (int m0 = 0; m0 < 8; m0 += MS) {
@@ -404,10 +422,24 @@ __device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][
         floatx4 acc = S[t][m0 + mm];
         acc[0] *= gam[mm].x; acc[1] *= gam[mm].y; acc[2] *= gam[mm].z; acc[3] *= gam[mm].w;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(krt[mm][kb], ub[t][kb], acc);
+        for (int kb = 0; kb < 2; ++kb) acc = mfma_bf16_k32(krt[mm][kb], R.ub[t][kb], acc);
         S[t][m0 + mm] = acc;
       }
   }
+}
+
+// The four phases back to back, from one image (the double-buffered kernel).
+// with_o = false skips O (segment pairs, whose images are copied without
+// Q_decay and M_qk).
+template <int NT>
+__device__ __forceinline__ void rec_step(const ChunkImage &im, floatx4 (&S)[NT][8], const bf16_t *V,
+                                         int vld, int vcol, bool with_o, __amdgpu_buffer_rsrc_t ro,
+                                         int off_o, int rowb, int g, int j) {
+  RecRegs<NT> R;
+  rec_phase0<NT>(im, S, V, vld, vcol, g, j, R);
+  rec_phase1<NT>(im, g, j, R);
+  if (with_o) rec_phase2<NT>(im, R, ro, off_o, rowb, g, j);
+  rec_phase3<NT>(im, S, R, g, j);
 }
 
 // The chunk a slot holds: document d, its index k in the document, first token
@@ -508,8 +540,8 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
 
   if (copier) {
     // ---------------- copy waves ----------------
-    const int cw = w - REC_COMPUTE_WAVES;                // 0..3
-    const int ct = tid - 64 * REC_COMPUTE_WAVES;         // 0..255
+    const int cw = w - REC_COMPUTE_WAVES;                // 0 .. REC_COPY_WAVES - 1
+    const int ct = tid - 64 * REC_COMPUTE_WAVES;         // 0 .. REC_COPY_THREADS - 1
     const bf16_t *v = (const bf16_t *)p.v;
     const char *img_h = (const char *)p.ws + (int64_t)h * p.n_slots * IMG_BYTES;
     const uint32_t lds_img = lds_addr(&sm.buf[0]);
@@ -528,21 +560,19 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
     constexpr int LPR = SLICE * ES / 16;
     constexpr int VROWS = 64 / LPR;
     constexpr int VBLOCKS = CH / VROWS;
-    static_assert(VBLOCKS % 4 == 0, "v blocks per copy wave");
-    // chunk of slot sl -> buffer kk & 1: v blocks cw, cw + 4, ..., the image in
-    // 1 KB blocks cw, cw + 4, ...
+    // chunk of slot sl -> buffer kk & 1: v blocks cw, cw + REC_COPY_WAVES, ...,
+    // the image in 1 KB blocks cw, cw + REC_COPY_WAVES, ...
     auto issue_copy = [&](int64_t sl, int kk) {
       const SlotChunk c = slot_chunk(p, sl);
       const i32x4 rv = v_rsrc(c, true);
       const uint32_t vdst = lds_v + (uint32_t)((kk & 1) * CH * SLICE * ES);
 #pragma unroll
-      for (int i = 0; i < VBLOCKS / 4; ++i) {
-        const int blk = cw + 4 * i;
+      for (int blk = cw; blk < VBLOCKS; blk += REC_COPY_WAVES) {
         copy16_to_lds(rv, vdst + blk * 1024, (VROWS * blk + lane / LPR) * rowb + (lane % LPR) * 16);
       }
       const i32x4 ri = rsrc_words(img_h + sl * IMG_BYTES, IMG_BYTES);
       const uint32_t dst = lds_img + (uint32_t)((kk & 1) * IMG_BYTES);
-      for (int blk = cw; blk < IMG_BLOCKS; blk += 4)
+      for (int blk = cw; blk < IMG_BLOCKS; blk += REC_COPY_WAVES)
         if (!(pairs_only && (in_blocks(blk, OFF_QD, OFF_KRT) || in_blocks(blk, OFF_MQK, OFF_INVB))))
           copy16_to_lds(ri, dst + blk * 1024, lane * 16 + blk * 1024);
     };
