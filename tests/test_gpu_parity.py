@@ -188,6 +188,43 @@ def test_chunk_fwd_is_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+@pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32", "unbounded", "checkpoints"])
+def test_final_state_in_place(path):
+    """kda_chunk_fwd and its variants may write the final states over the initial
+    states (each unit reads its initial state before it writes its final one):
+    O and the states equal the out-of-place call bit for bit.  The documents
+    include empty ones (final = initial, copied onto itself)."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    from kda_testlib import gpu_inputs
+    inp = kda_gen.make_prefill(36, 700, 3, "bf16", lengths=[130, 0, 257, 1, 0, 312],
+                               s0_std=0.05, s0_docs="all")
+    _case(inp, 1 if path == "fp32" else 0)
+    print(f"    path {path}", flush=True)
+    t = gpu_inputs(inp)
+    args = (t["q"], t["k"], t["v"], t["z"], t["beta"])
+
+    def run(S_in, fin):
+        if path == "unbounded":
+            return kda.kda_chunk_fwd_unbounded(*args, t["A_log"], S_in, t["cu"], t["cu_host"],
+                                               final_state=fin)[0]
+        if path == "checkpoints":
+            return kda.kda_chunk_fwd_checkpoints(*args, 128, t["A_log"], inp.g_min, S_in, t["cu"],
+                                                 t["cu_host"], final_state=fin)[0]
+        return kda.kda_chunk_fwd(*args, t["A_log"], inp.g_min, S_in, t["cu"], t["cu_host"],
+                                 compute=1 if path == "fp32" else 0,
+                                 workspace=False if path == "fused" else None, final_state=fin)[0]
+
+    S_out = torch.empty_like(t["S0"])
+    o_ref = kda_gen.from_torch(run(t["S0"], S_out))
+    S_io = t["S0"].clone()
+    o_in = kda_gen.from_torch(run(S_io, S_io))
+    torch.cuda.synchronize()
+    assert np.array_equal(o_in, o_ref)
+    assert np.array_equal(kda_gen.from_torch(S_io), kda_gen.from_torch(S_out))
+    assert np.array_equal(kda_gen.from_torch(S_io)[[1, 4]], inp.S0[[1, 4]])
+
+
 def test_chunk_fwd_resume_equals_one_call():
     """Splitting a document at a chunk-aligned token and carrying the final
     state gives the one-call result (the chunking is then identical)."""
