@@ -163,7 +163,9 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
       __syncthreads();
     }
 
-    for (int tt = 0; tt < nb; ++tt) {
+    // the last draft of a window is taken after the loop (no state update)
+    const bool last_draft = win.W2 > 0 && t0 + nb == ntok;
+    for (int tt = 0; tt < nb - (last_draft ? 1 : 0); ++tt) {
       const int t = t0 + tt;
       float kk[16], aa[16];
 #pragma unroll
@@ -242,6 +244,52 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                                       reinterpret_cast<floatx4 *>(Sg + (row0 + i) * D + col0));
           if ((i & 1) && i != 15 && meter) wait_vmem_except_last<1>();  // as the loads
         }
+      }
+    }
+    if (last_draft) {
+      // The last draft of the window: its state is not kept, so the update is
+      // not formed.  With S' = Diag(alpha) S and u = beta (v - S^T k), its
+      // output (S' + k u^T)^T q = S^T (alpha q) + (k^T q) u needs one pass over
+      // S (two weighted column sums) instead of decay, erase, update and read.
+      const int tt = nb - 1;
+      const int t = t0 + tt;
+      const float qsc = RAW ? s_qsc[tt] : 1.f, ksc = RAW ? s_ksc[tt] : 1.f;
+      float p[4] = {0.f, 0.f, 0.f, 0.f}, ob[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(&s_a[tt][row0 + i]);
+        const float4 k4 = *reinterpret_cast<const float4 *>(&s_k[tt][row0 + i]);
+        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[tt][row0 + i]);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+        const float kv[4] = {k4.x * ksc, k4.y * ksc, k4.z * ksc, k4.w * ksc};
+        const float qv[4] = {q4.x * qsc, q4.y * qsc, q4.z * qsc, q4.w * qsc};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ak = av[r] * kv[r], aq = av[r] * qv[r];
+          kq = fmaf(kv[r], qv[r], kq);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            p[c] = fmaf(s[i + r][c], ak, p[c]);
+            ob[c] = fmaf(s[i + r][c], aq, ob[c]);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 8; m < 64; m <<= 1) {
+        kq += __shfl_xor(kq, m);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          p[c] += __shfl_xor(p[c], m);
+          ob[c] += __shfl_xor(ob[c], m);
+        }
+      }
+      if (rg == 0) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(&s_v[tt][col0]);
+        const float bt = s_b[tt];
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ob[c] = fmaf(kq, bt * (vv[c] - p[c]), ob[c]);
+        io<Tin>::store4(win.o + (((int64_t)n * win.W2 + (t - acc - 1)) * H + h) * D + col0, ob);
       }
     }
     __syncthreads();  // the staging buffers are rewritten by the next batch

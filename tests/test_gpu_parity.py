@@ -633,12 +633,15 @@ def test_decode_skips_slots_outside_the_pool(W2):
     assert np.all(P[untouched] == 3.0)
 
 
-@pytest.mark.parametrize("dtype,W2", [("bf16", 4), ("f32", 4), ("bf16", 13)])
+@pytest.mark.parametrize("dtype,W2", [("bf16", 4), ("f32", 4), ("bf16", 13), ("f32", 1),
+                                      ("f32", 7)])
 def test_decode_window_matches_oracle(dtype, W2):
     """Replay + bonus + next draft window in one kernel: the bonus output and the
     state kept equal those of kda_decode_step bit for bit (the same arithmetic on
-    the same tokens), and the window drafts' outputs match the oracle.  W2 = 13
-    runs the token loop past two staging batches."""
+    the same tokens), and the window drafts' outputs match the oracle.  The last
+    draft of a window takes its own path (no state update): W2 = 1 makes it the
+    only draft, W2 = 7 puts it in the first staging batch or the second depending
+    on the accepted length, W2 = 13 runs the token loop past two batches."""
     import torch
     inp = kda_gen.make_decode(54, N=24, H=4, W=4, dtype=dtype,
                               accepted=[i % 5 for i in range(24)], W2=W2)
