@@ -40,3 +40,19 @@ def test_measured_traffic_follows_the_source_digest(tmp_path):
     # once the kernel sources change, the old figure no longer applies
     (tmp_path / "linear_attention_fwd_amd" / "csrc" / "k.hip").write_text("kernel v2")
     assert bench.measured_traffic(root, "kda_chunk_rec_kernel") is None
+
+
+def test_decode_byte_counts():
+    """State bytes: the fp32 state read and written per (sequence, head); total
+    adds 8D + 2 input bytes per replayed or window token and 2D output bytes per
+    output, per head."""
+    D = 128
+    assert bench.decode_state_bytes(512, 96) == 512 * 96 * D * D * 4 * 2
+    acc = [0, 4, 2]
+    tokens = (0 + 1) + (4 + 1) + (2 + 1)
+    H = 5
+    assert bench.decode_total_bytes(acc, H) == \
+        bench.decode_state_bytes(3, H) + H * tokens * (8 * D + 2) + 3 * H * 2 * D
+    # a window of W2 drafts adds their inputs and outputs
+    assert bench.decode_total_bytes(acc, H, W2=4) - bench.decode_total_bytes(acc, H) == \
+        3 * 4 * H * (8 * D + 2) + 3 * 4 * H * 2 * D
