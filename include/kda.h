@@ -143,7 +143,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk,
  * or T = 65536 at H = 4, fit; T = 8192 at H = 96 does not).  The scratch keeps
  * the last call's contents and needs no clearing (every call writes what it
  * reads).  Calls that overlap on one GPU (different streams, or host threads)
- * share the scratch and race: order them on one stream. */
+ * share the scratch and race: order them on one stream.  The scratch's address
+ * on a device is looked up by the first call there; make that first call
+ * outside any graph capture, after which calls capture and replay like the
+ * other entry points (they launch kernels only). */
 #define KDA_NOALLOC_SCRATCH_BYTES 268435456
 int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_logits,
                           const void *beta, const float *A_log, float g_min,
