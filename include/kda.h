@@ -27,12 +27,13 @@
  *     head) row of q and of k is scaled to unit L2 norm (an all-zero row stays
  *     zero) and beta is given as a logit, beta = Sigmoid(logit).  The bf16
  *     prefill rounds the normalised q and k rows to bf16, the precision of all
- *     its matrix operands; the decode step keeps them, and beta, in fp32.
- *     Accepted by the bf16 two-kernel prefill (kda_chunk_fwd with a workspace,
- *     kda_chunk_prep, kda_segment_scan with bf16 arithmetic,
- *     kda_chunk_fwd_checkpoints, kda_chunk_fwd_unbounded) and by the decode
- *     entry points; the fused and fp32-arithmetic prefill return
- *     KDA_ERR_UNSUPPORTED.  kda_chunk_recurrence ignores it (it reads v only).
+ *     its matrix operands; the fp32 prefill (fp32 inputs) and the decode step
+ *     keep them, and beta, in fp32.  Accepted by kda_chunk_fwd and
+ *     kda_chunk_fwd_unbounded (except bf16 inputs with fp32 arithmetic:
+ *     KDA_ERR_UNSUPPORTED), kda_chunk_prep, kda_chunk_fwd_checkpoints,
+ *     kda_chunk_fwd_noalloc, kda_segment_scan (with the same exception) and
+ *     the decode entry points.  kda_chunk_recurrence ignores it (it reads v
+ *     only).
  *   * The caller owns every buffer, including workspaces.  The library never
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream).  Return codes describe
@@ -223,8 +224,11 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
  * cores (same section): they are computed per position pair in fp32, the
  * path whose cost the bounded gate removes; every other step is the one of
  * kda_chunk_fwd.  Arguments as for kda_chunk_fwd without g_min and compute:
- * bf16 inputs only (KDA_ERR_UNSUPPORTED otherwise), two-kernel path, a
- * workspace of kda_chunk_fwd_workspace_size() bytes required. */
+ * bf16 inputs with a workspace of kda_chunk_fwd_workspace_size() bytes run the
+ * two-kernel path, bf16 inputs with a NULL workspace the fused kernel (both
+ * bf16 arithmetic), fp32 inputs the fused kernel in fp32 arithmetic (the
+ * verification build; the workspace is not touched).  The fp32 build forms
+ * the per-position subtiles from fp32 q and k. */
 int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const void *g_logits,
                             const void *beta, const float *A_log, const float *initial_state,
                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N,

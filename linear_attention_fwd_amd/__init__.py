@@ -259,8 +259,10 @@ def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=N
                             cu_seqlens=None, cu_seqlens_host=None,
                             output_final_state: bool = True, o=None, final_state=None,
                             workspace=None, raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
-    """``kda_chunk_fwd`` with the unbounded gate g = -exp(A_h) softplus(z) (bf16
-    inputs, two-kernel path).  Returns (o, final_state) as ``kda_chunk_fwd``."""
+    """``kda_chunk_fwd`` with the unbounded gate g = -exp(A_h) softplus(z).  bf16
+    inputs run the two-kernel path with a workspace (None allocates one) or the
+    fused kernel (``workspace=False``); fp32 inputs run the fused kernel in fp32
+    arithmetic.  Returns (o, final_state) as ``kda_chunk_fwd``."""
     torch = _torch()
     lib = load_library()
     T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
@@ -271,14 +273,15 @@ def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=N
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(max(1, kda_chunk_fwd_workspace_size(N, T, H, dk, dv)),
-                                dtype=torch.uint8, device=q.device)
+                                dtype=torch.uint8, device=q.device) \
+            if _dtype_code(q) == KDA_BF16 else False
+    ws_ptr, ws_bytes = (None, 0) if workspace is False else \
+        (_ptr(workspace), workspace.numel() * workspace.element_size())
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_unbounded(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
                                      _ptr(A_log), _ptr(initial_state), _ptr(cu_dev), host_ptr, N,
                                      T, H, dk, dv, _dtype_code(q, raw_inputs), _ptr(o),
-                                     _ptr(final_state),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream())
+                                     _ptr(final_state), ws_ptr, ws_bytes, _stream())
     _check(rc)
     return o, final_state
 

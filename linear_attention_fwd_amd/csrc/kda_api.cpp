@@ -42,7 +42,9 @@ bool take_raw_flag(int32_t &dtype) {
   return raw;
 }
 int raw_unsupported(const char *who) {
-  return fail(KDA_ERR_UNSUPPORTED, "%s: KDA_RAW_INPUTS needs the bf16 two-kernel path", who);
+  return fail(KDA_ERR_UNSUPPORTED,
+              "%s: raw inputs with fp32 arithmetic need fp32 inputs (bf16 inputs would be "
+              "normalised into bf16 operands)", who);
 }
 
 // Sizes, dtype and document offsets shared by the prefill entry points.
@@ -238,7 +240,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
   if (rc != KDA_OK) return rc;
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   const bool split = workspace != nullptr && !f32c;
-  if (raw && !split) return raw_unsupported("kda_chunk_fwd");
+  if (raw && f32c && dtype == KDA_BF16) return raw_unsupported("kda_chunk_fwd");
   if (split) {
     rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
     if (rc != KDA_OK) return rc;
@@ -260,7 +262,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
     p.mode = 0; p.n_items = N; p.seg_len = 0;
     p.item_init = initial_state; p.doc_init = nullptr;
     p.o = o; p.final_state = final_state;
-    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, f32c, st);
+    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, f32c, kda::GATE_BOUNDED, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
@@ -364,12 +366,15 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
   int rc = check_prefill(q, k, v, g_logits, beta, unused_g_min, cu_seqlens, cu_seqlens_host, N, T,
                          H, dk, dv, dtype, KDA_COMPUTE_AUTO, o);
   if (rc != KDA_OK) return rc;
-  if (dtype != KDA_BF16)
-    return fail(KDA_ERR_UNSUPPORTED, "the unbounded gate runs on the bf16 two-kernel path only");
-  rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
-  if (rc != KDA_OK) return rc;
+  // bf16 inputs with a workspace: the two-kernel path; without one: the fused
+  // kernel (bf16 arithmetic); fp32 inputs: the fused kernel in fp32 arithmetic
+  const bool split = dtype == KDA_BF16 && workspace != nullptr;
+  if (split) {
+    rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
+    if (rc != KDA_OK) return rc;
+  }
   hipStream_t st = (hipStream_t)stream;
-  if (T > 0) {
+  if (T > 0 && split) {
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, unused_g_min, initial_state,
                                       cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
                                       workspace);
@@ -377,6 +382,17 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
     p.raw = raw;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
+    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
+  } else if (T > 0) {
+    kda::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
+    p.A_log = A_log; p.g_min = unused_g_min;
+    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
+    p.mode = 0; p.n_items = N; p.seg_len = 0;
+    p.item_init = initial_state; p.doc_init = nullptr;
+    p.o = o; p.final_state = final_state;
+    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, dtype == KDA_F32, kda::GATE_SOFTPLUS,
+                                   raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
@@ -481,7 +497,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
       return fail(KDA_ERR_UNSUPPORTED, "kda_segment_scan: final_state must not overlap initial_state");
   }
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
-  if (raw && f32c) return raw_unsupported("kda_segment_scan");
+  if (raw && f32c && dtype == KDA_BF16) return raw_unsupported("kda_segment_scan");
   int64_t req = n_segments;
   if (req <= 0) {
     const int cus = kda_default_segments();
@@ -577,7 +593,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     p.doc_init = initial_state;
     // A: segment pairs (M, S~)
     p.mode = 2; p.item_init = nullptr; p.o = nullptr; p.final_state = pairs;
-    hipError_t e = kda::launch_fwd(p, bf16_in, f32c, st);
+    hipError_t e = kda::launch_fwd(p, bf16_in, f32c, kda::GATE_BOUNDED, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states
     e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, H, (int)sp.n_seg, sp.len,
@@ -585,7 +601,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
     // C: re-run every segment from its exact entry state
     p.mode = 1; p.item_init = entry; p.o = o; p.final_state = final_state;
-    e = kda::launch_fwd(p, bf16_in, f32c, st);
+    e = kda::launch_fwd(p, bf16_in, f32c, kda::GATE_BOUNDED, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {

@@ -27,6 +27,7 @@
 // hand their recurrence operands to a sink functor.
 #pragma once
 #include "kda_device.h"
+#include <type_traits>
 #include "kda_launch.h"
 
 namespace kda {
@@ -250,6 +251,28 @@ __device__ __forceinline__ void l2norm_rows(bufio<bf16_t>::raw8 (&R)[4]) {
     const bf16x8 y = to_bf16x8(floatx8{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc, x[4] * sc,
                                        x[5] * sc, x[6] * sc, x[7] * sc});
     R[r].a = __builtin_bit_cast(u32x4, y);
+  }
+}
+// The same on fp32 inputs: the rows stay in fp32 (the precision of the fp32
+// build's operands).
+__device__ __forceinline__ void l2norm_rows(bufio<float>::raw8 (&R)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x[8];
+    bufio<float>::cvt8(R[r], x);
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(x[c], x[c], ss);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 8);
+    const float sc = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      R[r].a[i] = __float_as_uint(x[i] * sc);
+      R[r].b[i] = __float_as_uint(x[4 + i] * sc);
+    }
   }
 }
 
@@ -495,24 +518,35 @@ __device__ __forceinline__ void wave_lds_sync() {
 //   M_qk[i][j] = sum_c q_ic k_jc e^(G_ic - G_jc),
 //   L[i][j]    = beta_i sum_c k_ic k_jc e^(G_ic - G_jc)   (j < i only),
 // where e^(G_ic - G_jc) <= 1 never overflows.  The wave stages its tokens'
-// q, k (bf16, as read) and G (fp32) in `stage` (8 KB of LDS of its own), 64
-// channels at a time.  Lane (tq, cg) takes subtile rows tq, 7 - tq, 8 + tq and
-// 15 - tq (34 position pairs for every lane) and channels 4cg..4cg+3 of each
-// half; the channel sums are then spread over the 16 lanes of the row group,
-// lane cg keeping column cg.  M_qk goes to mqk_sink(row, col, value) (zeros
-// above the diagonal included), L to the L tile.
-template <class MqkSink>
+// q, k (as read: bf16 or fp32) and G (fp32) in `stage` (LDS of its own,
+// diag_stage_bytes: 8 KB for bf16 inputs, 12 KB for fp32), 64 channels at a
+// time.  Lane (tq, cg) takes subtile rows tq, 7 - tq, 8 + tq and 15 - tq (34
+// position pairs for every lane) and channels 4cg..4cg+3 of each half; the
+// channel sums are then spread over the 16 lanes of the row group, lane cg
+// keeping column cg.  M_qk goes to mqk_sink(row, col, value) (zeros above the
+// diagonal included), L to the L tile in the operand precision of Ar.
+template <class IO> constexpr int diag_stage_bytes() { return 16 * 64 * (4 + 2 * IO::ES); }
+template <class IO, class Ar, class MqkSink>
 __device__ __forceinline__ void prep_diag_positions(char *stage,
-                                                    const bufio<bf16_t>::raw8 (&Rq)[4],
-                                                    const bufio<bf16_t>::raw8 (&Rk)[4],
+                                                    const typename IO::raw8 (&Rq)[4],
+                                                    const typename IO::raw8 (&Rk)[4],
                                                     const float (&G)[4][8], const float *beta,
-                                                    bf16_t *L, int w, int tq, int cg,
+                                                    typename Ar::E *L, int w, int tq, int cg,
                                                     MqkSink &&mqk_sink) {
-  using TL = Tile<bf16_t, CH>;
+  using TL = Tile<typename Ar::E, CH>;
+  using SE = typename std::conditional<IO::ES == 2, bf16_t, float>::type;  // staged q, k
   constexpr int HC = 64;  // channels staged at a time
-  float *Gs = reinterpret_cast<float *>(stage);              // [16][HC]
-  bf16_t *Qs = reinterpret_cast<bf16_t *>(stage + 16 * HC * 4);  // [16][HC]
-  bf16_t *Ks = Qs + 16 * HC;                                     // [16][HC]
+  float *Gs = reinterpret_cast<float *>(stage);               // [16][HC]
+  SE *Qs = reinterpret_cast<SE *>(stage + 16 * HC * 4);       // [16][HC]
+  SE *Ks = Qs + 16 * HC;                                      // [16][HC]
+  auto load4 = [](const SE *x) {
+    if constexpr (IO::ES == 2) {
+      return Arith<false>::load4(x);
+    } else {
+      const float4 f = *reinterpret_cast<const float4 *>(x);
+      return floatx4{f.x, f.y, f.z, f.w};
+    }
+  };
   const int c0 = 4 * cg;
 #pragma unroll 1
   for (int s = 0; s < 4; ++s) {
@@ -532,20 +566,27 @@ __device__ __forceinline__ void prep_diag_positions(char *stage,
           const int i = 4 * tq + r;
           *reinterpret_cast<float4 *>(&Gs[i * HC + lc]) = make_float4(G[r][0], G[r][1], G[r][2], G[r][3]);
           *reinterpret_cast<float4 *>(&Gs[i * HC + lc + 4]) = make_float4(G[r][4], G[r][5], G[r][6], G[r][7]);
-          *reinterpret_cast<u32x4 *>(&Qs[i * HC + lc]) = Rq[r].a;
-          *reinterpret_cast<u32x4 *>(&Ks[i * HC + lc]) = Rk[r].a;
+          if constexpr (IO::ES == 2) {
+            *reinterpret_cast<u32x4 *>(&Qs[i * HC + lc]) = Rq[r].a;
+            *reinterpret_cast<u32x4 *>(&Ks[i * HC + lc]) = Rk[r].a;
+          } else {
+            *reinterpret_cast<u32x4 *>(&Qs[i * HC + lc]) = Rq[r].a;
+            *reinterpret_cast<u32x4 *>(&Qs[i * HC + lc + 4]) = Rq[r].b;
+            *reinterpret_cast<u32x4 *>(&Ks[i * HC + lc]) = Rk[r].a;
+            *reinterpret_cast<u32x4 *>(&Ks[i * HC + lc + 4]) = Rk[r].b;
+          }
         }
       }
       wave_lds_sync();
       const float4 gi = *reinterpret_cast<const float4 *>(&Gs[row * HC + c0]);
-      const floatx4 qi = Arith<false>::load4(&Qs[row * HC + c0]);
-      const floatx4 ki = Arith<false>::load4(&Ks[row * HC + c0]);
+      const floatx4 qi = load4(&Qs[row * HC + c0]);
+      const floatx4 ki = load4(&Ks[row * HC + c0]);
       const float giv[4] = {gi.x, gi.y, gi.z, gi.w};
 #pragma unroll
       for (int jj = 0; jj < NJ_MAX; ++jj) {
         if (jj < nj) {
           const float4 gj = *reinterpret_cast<const float4 *>(&Gs[jj * HC + c0]);
-          const floatx4 kj = Arith<false>::load4(&Ks[jj * HC + c0]);
+          const floatx4 kj = load4(&Ks[jj * HC + c0]);
           const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
           const bool lower = jj <= row;
 #pragma unroll
@@ -563,7 +604,7 @@ __device__ __forceinline__ void prep_diag_positions(char *stage,
     const float lv = reduce_scatter16(l, cg);
     const int i = 16 * w + row;
     mqk_sink(i, 16 * w + cg, mv);
-    L[TL::idx(i, 16 * w + cg)] = f32_to_bf16(cg < row ? beta[i] * lv : 0.f);
+    L[TL::idx(i, 16 * w + cg)] = Ar::cvt(cg < row ? beta[i] * lv : 0.f);
   }
 }
 

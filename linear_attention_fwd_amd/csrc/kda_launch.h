@@ -27,8 +27,14 @@ struct FwdParams {
                            // [n_items, H, D, 2D] (columns 0..127 = S~, 128..255 = M)
   int nsplit;              // set by the launcher
 };
+constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
 
-hipError_t launch_fwd(FwdParams p, bool bf16_in, bool f32_compute, hipStream_t stream);
+// gate: GATE_BOUNDED or GATE_SOFTPLUS (the unbounded gate, g_min unused); raw:
+// q, k L2-normalised and the beta sigmoid in the kernel.  Raw inputs with bf16
+// inputs and fp32 arithmetic are not supported (the normalised rows would be
+// rounded to bf16); the caller refuses them.
+hipError_t launch_fwd(FwdParams p, bool bf16_in, bool f32_compute, int gate, bool raw,
+                      hipStream_t stream);
 
 // Chunk slots: chunk k of document d (chunks of 64 tokens restart at every
 // document start) lives in slot  first_slot(cu[d], d) + k  with
@@ -79,7 +85,6 @@ struct SplitParams {
   // nullptr = input order
   int32_t *order;
 };
-constexpr int GATE_BOUNDED = 0, GATE_SOFTPLUS = 1;
 // Bytes of one chunk image (the recurrence operands of one (head, chunk);
 // the layout is ChunkImage in kda_split.hip, which checks this size).
 constexpr int64_t CHUNK_IMAGE_BYTES = 63488;

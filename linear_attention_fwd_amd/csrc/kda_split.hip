@@ -157,9 +157,9 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
   const __amdgpu_buffer_rsrc_t ri =
       make_rsrc((char *)p.ws + ((int64_t)h * p.n_slots + slot) * IMG_BYTES, IMG_BYTES);
   if constexpr (UNB) {
-    static_assert(sizeof(sm.u) >= 4 * 8192, "per-wave staging for the diagonal subtiles");
+    static_assert(sizeof(sm.u) >= 4 * diag_stage_bytes<IO>(), "per-wave staging for the diagonal subtiles");
     if (!diag_two_factor(sm.ps, w))  // else the subtile products form it
-      prep_diag_positions(reinterpret_cast<char *>(&sm.u) + w * 8192, Rq, Rk, G, sm.ps.beta, sm.L,
+      prep_diag_positions<IO, Ar>(reinterpret_cast<char *>(&sm.u) + w * diag_stage_bytes<IO>(), Rq, Rk, G, sm.ps.beta, sm.L,
                         w, tq, cg, [&](int row, int col, float m) {
                           __builtin_amdgcn_raw_buffer_store_b16(
                               f32_to_bf16(m), ri, OFF_MQK + 2 * PackedLower::idx(row, kperm(col)), 0, 0);

@@ -128,13 +128,15 @@ def gpu_chunk_fwd(inp, compute=0, t=None, fused=False):
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 
 
-def gpu_chunk_fwd_unbounded(inp, t=None):
-    """kda_chunk_fwd_unbounded (softplus gate) on the GPU."""
+def gpu_chunk_fwd_unbounded(inp, t=None, fused=False):
+    """kda_chunk_fwd_unbounded (softplus gate) on the GPU: the two-kernel path for
+    bf16 inputs (fused=True: the fused kernel), the fp32 fused kernel for fp32."""
     import linear_attention_fwd_amd as kda
     import torch
     t = t or gpu_inputs(inp)
     o, S = kda.kda_chunk_fwd_unbounded(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
-                                       t["S0"], t["cu"], t["cu_host"], raw_inputs=inp.raw)
+                                       t["S0"], t["cu"], t["cu_host"], raw_inputs=inp.raw,
+                                       workspace=False if fused else None)
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 

@@ -73,6 +73,22 @@ int main() {
   EXPECT(kda_chunk_fwd_unbounded(F, F, F, F, F, Ff, Ff, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16,
                                  F, Ff, F, ws, nullptr),
          KDA_ERR_HIP);
+  // the fused kernel: raw inputs, the unbounded gate, fp32 inputs
+  EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                       KDA_BF16 | KDA_RAW_INPUTS, 0, F, Ff, nullptr, 0, nullptr),
+         KDA_ERR_HIP);
+  EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                       KDA_F32 | KDA_RAW_INPUTS, 0, F, Ff, nullptr, 0, nullptr),
+         KDA_ERR_HIP);
+  EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                       KDA_BF16 | KDA_RAW_INPUTS, KDA_COMPUTE_F32, F, Ff, nullptr, 0, nullptr),
+         KDA_ERR_UNSUPPORTED);  // bf16 inputs normalised into fp32 arithmetic
+  EXPECT(kda_chunk_fwd_unbounded(F, F, F, F, F, Ff, Ff, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16,
+                                 F, Ff, nullptr, 0, nullptr),
+         KDA_ERR_HIP);
+  EXPECT(kda_chunk_fwd_unbounded(F, F, F, F, F, Ff, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                                 KDA_F32 | KDA_RAW_INPUTS, F, Ff, nullptr, 0, nullptr),
+         KDA_ERR_HIP);
   {
     const int interval = 128;
     const size_t nck = kda_checkpoint_count(N, T, interval);
@@ -99,6 +115,17 @@ int main() {
     EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -5.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
                             KDA_F32, 0, n_seg, F, Ff, F, sws, nullptr),
            KDA_ERR_HIP);
+    // raw inputs on either path, except bf16 inputs with fp32 arithmetic
+    EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -5.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
+                            KDA_BF16 | KDA_RAW_INPUTS, 0, n_seg, F, Ff, F, sws, nullptr),
+           KDA_ERR_HIP);
+    EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -5.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
+                            KDA_F32 | KDA_RAW_INPUTS, 0, n_seg, F, Ff, F, sws, nullptr),
+           KDA_ERR_HIP);
+    EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -5.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
+                            KDA_BF16 | KDA_RAW_INPUTS, KDA_COMPUTE_F32, n_seg, F, Ff, F, sws,
+                            nullptr),
+           KDA_ERR_UNSUPPORTED);
     EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -5.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
                             KDA_BF16, 0, n_seg, F, Ff, F, 1024, nullptr),
            KDA_ERR_WORKSPACE);

@@ -26,7 +26,7 @@ static hipError_t launched() {
   ++g_launches;
   return hipErrorInvalidValue;
 }
-hipError_t launch_fwd(FwdParams, bool, bool, hipStream_t) { return launched(); }
+hipError_t launch_fwd(FwdParams, bool, bool, int, bool, hipStream_t) { return launched(); }
 hipError_t launch_chunk_prep(const SplitParams &, hipStream_t) { return launched(); }
 hipError_t launch_chunk_recurrence(const SplitParams &, hipStream_t) { return launched(); }
 hipError_t launch_copy_empty(const int32_t *, int64_t, const float *, float *, int, int,

@@ -233,18 +233,19 @@ def test_decode_validation(lib):
 
 
 def test_raw_inputs_flag(lib):
-    """KDA_RAW_INPUTS is accepted where the two-kernel prep or the decode kernel
-    runs and refused on the fused and fp32 prefill; other bits are unknown."""
+    """KDA_RAW_INPUTS is refused only where the normalised rows would lose
+    precision (bf16 inputs into fp32 arithmetic); other bits are unknown.  (The accepted combinations would launch kernels, so
+    they are driven here only by the sanitizer build against stub launchers.)"""
     RAW = kda.KDA_RAW_INPUTS
     def fwd(dtype, ws, compute=0):
         return lib.kda_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1,
                                  256, 4, 128, 128, dtype, compute, FAKE, None, ws,
                                  1 << 30 if ws else 0, None)
-    assert fwd(1 | RAW, None) == KDA_ERR_UNSUPPORTED         # fused path (no workspace)
-    assert fwd(1 | RAW, FAKE, compute=1) == KDA_ERR_UNSUPPORTED  # fp32 arithmetic
-    assert fwd(0 | RAW, FAKE) == KDA_ERR_UNSUPPORTED         # fp32 inputs
+    assert fwd(1 | RAW, FAKE, compute=1) == KDA_ERR_UNSUPPORTED  # bf16 in, fp32 arithmetic
+    assert fwd(1 | RAW, None, compute=1) == KDA_ERR_UNSUPPORTED
     assert fwd(1 | 0x200, FAKE) == KDA_ERR_DTYPE              # unknown bit
     for n_seg in (0, 7):  # refused before the device is asked for its compute units
+        # (bf16 inputs, fp32 arithmetic)
         assert lib.kda_segment_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1,
                                     256, 4, 128, 128, 1 | RAW, 1, n_seg, FAKE, None, FAKE, 1 << 30,
                                     None) == KDA_ERR_UNSUPPORTED
@@ -263,9 +264,9 @@ def test_unbounded_validation(lib):
                                            a["T"], a["H"], 128, 128, a["dtype"], FAKE, None,
                                            a["ws"], a["ws_bytes"], None)
     assert call(q=None) == KDA_ERR_NULL
-    assert call(dtype=0) == KDA_ERR_UNSUPPORTED     # fp32 inputs: bf16 path only
-    assert call(ws=None) == KDA_ERR_WORKSPACE
-    assert call(ws_bytes=100) == KDA_ERR_WORKSPACE
+    assert call(ws_bytes=100) == KDA_ERR_WORKSPACE  # a workspace given must be large enough
+    assert call(dtype=0, H=0) == KDA_ERR_SHAPE      # fp32 inputs (fused kernel) validated too
+    assert call(dtype=0, q=None) == KDA_ERR_NULL
     assert call(H=0) == KDA_ERR_SHAPE
 
 

@@ -482,12 +482,17 @@ def _diagonal_subtile_forms(inp):
     return within, beyond
 
 
+@pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32"])
 @pytest.mark.parametrize("name", sorted(UNBOUNDED_CASES))
-def test_unbounded_gate_matches_oracle(name):
+def test_unbounded_gate_matches_oracle(name, path):
+    """The unbounded gate on the bf16 two-kernel path and the bf16 fused kernel
+    (1e-2), and on fp32 inputs through the fp32 verification build (1e-4), which
+    forms the same two-factor and per-position diagonal subtiles in fp32."""
     c = dict(UNBOUNDED_CASES[name])
     seed, T, H = c.pop("seed"), c.pop("T"), c.pop("H")
-    inp = kda_gen.make_prefill(seed, T, H, "bf16", gate="softplus", **c)
-    print(f"[case] unbounded gate {name} T={T} H={H} N={inp.N}", flush=True)
+    dtype = "f32" if path == "fp32" else "bf16"
+    inp = kda_gen.make_prefill(seed, T, H, dtype, gate="softplus", **c)
+    print(f"[case] unbounded gate {name} T={T} H={H} N={inp.N} path {path}", flush=True)
     within, beyond = _diagonal_subtile_forms(inp)
     print(f"    diagonal subtile-heads: {within} two-factor, {beyond} per position", flush=True)
     if name == "strong_decay_varlen":
@@ -495,12 +500,20 @@ def test_unbounded_gate_matches_oracle(name):
         assert (G[0] - G[15]).max() > 100.0  # e^100 is beyond fp32
     assert within > 0 and (beyond > 0) == (name != "single_ragged_1000")
     o_ref, S_ref = oracle_forward(inp)
-    o, S = gpu_chunk_fwd_unbounded(inp)
+    o, S = gpu_chunk_fwd_unbounded(inp, fused=path == "fused")
     assert np.isfinite(o).all() and np.isfinite(S).all()
     eo, _ = rel_l2_slices(o, o_ref, inp.cu_seqlens)
     es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
     print(f"    o: {eo:.3e}  state: {es:.3e}", flush=True)
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    tol = TOL_F32 if path == "fp32" else TOL_BF16
+    assert eo <= tol and es <= tol
+    if path == "fused":  # the same stages as the two kernels
+        o2, S2 = gpu_chunk_fwd_unbounded(inp)
+        print(f"    identical to the two-kernel path: O {np.array_equal(o, o2)}, "
+              f"S {np.array_equal(S, S2)}", flush=True)
+        eo2, _ = rel_l2_slices(o, o2, inp.cu_seqlens)
+        es2, _ = rel_l2_slices(S, S2, axis_tokens=False)
+        assert eo2 <= 1e-3 and es2 <= 1e-3, (eo2, es2)
 
 
 # ---------------------------------------------------------------------------
@@ -511,26 +524,30 @@ def _zero_rows(t, rows):
     return t
 
 
-@pytest.mark.parametrize("path", ["chunk_fwd", "segment_scan", "unbounded"])
+@pytest.mark.parametrize("path", ["chunk_fwd", "segment_scan", "unbounded", "fused",
+                                  "unbounded_fused", "fp32", "segment_scan_fp32",
+                                  "unbounded_fp32"])
 def test_raw_inputs_prefill(path):
     """Unnormalised q, k and beta logits through the two-kernel prefill (and the
-    segment scan and the unbounded gate, which share its prep), against the
-    oracle that normalises them.  Some tokens have all-zero q or k rows (their
+    segment scan and the unbounded gate, which share its prep), the fused kernel
+    (bf16), and the fp32 verification build on fp32 inputs (1e-4; documents and
+    segments), against the oracle that normalises them.  Some tokens have all-zero q or k rows (their
     normalised rows stay zero)."""
-    inp = kda_gen.make_prefill(64, 1200, 4, "bf16", lengths=[500, 0, 77, 623], s0_std=0.05,
+    dtype = "f32" if path.endswith("fp32") else "bf16"
+    inp = kda_gen.make_prefill(64, 1200, 4, dtype, lengths=[500, 0, 77, 623], s0_std=0.05,
                                s0_docs="all", raw=True,
-                               gate="softplus" if path == "unbounded" else "bounded")
+                               gate="softplus" if path.startswith("unbounded") else "bounded")
     _zero_rows(inp.q, [3, 600, 1199])
     _zero_rows(inp.k, [4, 577, 1000])
     _case(inp, 0)
     print(f"    raw inputs, {path}", flush=True)
     o_ref, S_ref = oracle_forward(inp)
-    if path == "chunk_fwd":
-        o, S = gpu_chunk_fwd(inp)
-    elif path == "segment_scan":
+    if path in ("chunk_fwd", "fused", "fp32"):
+        o, S = gpu_chunk_fwd(inp, fused=path == "fused")
+    elif path.startswith("segment_scan"):
         o, S = gpu_segment_scan(inp, n_segments=7)
     else:
-        o, S = gpu_chunk_fwd_unbounded(inp)
+        o, S = gpu_chunk_fwd_unbounded(inp, fused=path == "unbounded_fused")
     assert np.all(o[[3, 600, 1199]] == 0)
     _check_prefill(inp, o, S, _tols(inp, 0))
 
