@@ -428,36 +428,52 @@ UNBOUNDED_CASES = {
 }
 
 
-def test_unbounded_gate_single_token_and_empty_document():
+@pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32"])
+def test_unbounded_gate_single_token_and_empty_document(path):
     """The unbounded gate on a one-token document beside an empty one and a
-    ragged 70-token one: partial chunks pad with zeros, the empty document passes
-    its initial state through."""
-    inp = kda_gen.make_prefill(63, 71, 2, "bf16", lengths=[1, 0, 70], s0_std=0.05,
+    ragged 70-token one, on each prefill path (fp32: fp32 inputs): partial chunks
+    pad with zeros, the empty document passes its initial state through."""
+    dtype = "f32" if path == "fp32" else "bf16"
+    inp = kda_gen.make_prefill(63, 71, 2, dtype, lengths=[1, 0, 70], s0_std=0.05,
                                s0_docs="all", gate="softplus")
     _case(inp, 0)
-    o, S = gpu_chunk_fwd_unbounded(inp)
+    print(f"    path {path}", flush=True)
+    o, S = gpu_chunk_fwd_unbounded(inp, fused=path == "fused")
     _check_prefill(inp, o, S, _tols(inp, 0))
     assert np.array_equal(S[1], inp.S0[1])
 
 
 def test_all_documents_empty():
     """T = 0: nothing to run, every final state is the document's initial state
-    (chunk kernels, segment scan and the unbounded gate)."""
+    (chunk kernels, segment scan and the unbounded gate, bf16 and fp32 inputs,
+    with and without a workspace)."""
     import torch
     import linear_attention_fwd_amd as kda
     H = 2
     S0 = np.random.default_rng(67).standard_normal((3, H, 128, 128)).astype(np.float32)
     z = torch.zeros((0, H, 128), dtype=torch.bfloat16, device="cuda")
     b = torch.zeros((0, H), dtype=torch.bfloat16, device="cuda")
+    zf, bf = z.float(), b.float()
     s0 = torch.from_numpy(S0).cuda()
     cu_host = np.zeros(4, dtype=np.int32)
     cu = torch.from_numpy(cu_host).cuda()
     print("[case] T=0, 3 empty documents", flush=True)
     for name, call in (
             ("chunk_fwd", lambda: kda.kda_chunk_fwd(z, z, z, z, b, None, -5.0, s0, cu, cu_host)),
+            ("chunk_fwd fused", lambda: kda.kda_chunk_fwd(z, z, z, z, b, None, -5.0, s0, cu, cu_host,
+                                                          workspace=False)),
+            ("chunk_fwd fp32", lambda: kda.kda_chunk_fwd(zf, zf, zf, zf, bf, None, -5.0, s0, cu,
+                                                         cu_host)),
             ("segment_scan", lambda: kda.kda_segment_scan(z, z, z, z, b, None, -5.0, s0, cu, cu_host,
                                                           n_segments=4)),
-            ("unbounded", lambda: kda.kda_chunk_fwd_unbounded(z, z, z, z, b, None, s0, cu, cu_host))):
+            ("segment_scan fp32", lambda: kda.kda_segment_scan(zf, zf, zf, zf, bf, None, -5.0, s0, cu,
+                                                               cu_host, n_segments=4)),
+            ("unbounded", lambda: kda.kda_chunk_fwd_unbounded(z, z, z, z, b, None, s0, cu, cu_host)),
+            ("unbounded fused", lambda: kda.kda_chunk_fwd_unbounded(z, z, z, z, b, None, s0, cu, cu_host,
+                                                                    workspace=False)),
+            ("unbounded fp32", lambda: kda.kda_chunk_fwd_unbounded(zf, zf, zf, zf, bf, None, s0, cu,
+                                                                   cu_host))):
+        print(f"    {name}", flush=True)
         o, S = call()
         torch.cuda.synchronize()
         assert o.shape == (0, H, 128)
