@@ -201,7 +201,9 @@ __device__ __forceinline__ void touch4_to_lds(i32x4 rsrc, uint32_t lds_addr, int
 // s_waitcnt vmcnt(0): all vector memory operations of this wave have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N): all but the N most recently issued vector memory
-// operations of this wave have completed (they complete in issue order).
+// operations of this wave have completed.  That holds for operations of one
+// kind, which complete in issue order; loads and stores share the counter but
+// not that order, so every caller has only loads (or only stores) in flight.
 template <int N> __device__ __forceinline__ void wait_vmem_except_last() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -605,6 +605,9 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
                     ct < CH * VLINES ? (ct / VLINES) * rowb + (ct % VLINES) * TOUCH_LINE : OOB);
     };
     constexpr int AHEAD = 2;  // slots between a touch and the copy that uses it
+    // The wait at the top of the loop leaves one touch batch in flight: one must
+    // have been issued after every copy, the first included.
+    static_assert(AHEAD >= 2, "a touch batch follows every copy");
 
     int64_t sl = next_chunk_slot(p, s_begin, s_end);
     if (sl < s_end) issue_copy(sl, 0);
@@ -656,9 +659,9 @@ __global__ void __launch_bounds__(REC_THREADS, 1) kda_chunk_rec_kernel(SplitPara
 #pragma unroll
         for (int t = 0; t < NT; ++t) state_load(S[t], s0, D, colW + 16 * t, g, j);
         // Wait for these loads here.  Left to the compiler, the wait falls
-        // where this branch rejoins the loop and, loads and stores completing
-        // in issue order, would hold every chunk until the previous chunk's O
-        // stores had reached memory.
+        // where this branch rejoins the loop, on every chunk; with the previous
+        // chunk's O stores pending on the same counter it must wait for those
+        // too, and would hold every chunk until they had reached memory.
         wait_vmem();
       } else {
 #pragma unroll
