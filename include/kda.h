@@ -41,8 +41,13 @@
  *   * Every argument the host can check is checked before any HIP call;
  *     failures return a negative kda_status and enqueue nothing.
  *   * Sizes: H <= 65535 heads and T < 2^31 tokens (the kernels address one
- *     64-token chunk of one head with 32-bit offsets); larger values return
- *     KDA_ERR_SHAPE.
+ *     64-token chunk of one head with 32-bit offsets), and every launch within
+ *     one dispatch's 2^32 - 1 work-items: for the prefill entry points
+ *     N * H <= 8388600 and (T / 64 + N) * H <= 16777215 (chunk slots x heads),
+ *     for kda_segment_scan also n_segments * H <= 4194296 (e.g. at most 64
+ *     segments at H = 65535, so the default of one per compute unit needs
+ *     H <= 16383), and for the decode entry points N * H <= 16777215.  Larger
+ *     values return KDA_ERR_SHAPE.
  *   * Values the host cannot see (device-resident lengths) are clamped in the
  *     kernel and reported through an optional device error flag.
  *   * No C++ exception crosses this interface.  kda_last_error() returns a

@@ -34,6 +34,22 @@ constexpr int kC = 64;  // chunk length
 // byte offsets: up to 64 tokens x H heads x 128 channels x 4 bytes.
 constexpr int kMaxHeads = 65535;
 static_assert((int64_t)kC * kMaxHeads * kD * 4 <= (int64_t)INT32_MAX, "chunk offsets fit int32");
+// One dispatch covers at most 2^32 - 1 work-items (grid x workgroup size).
+// Every grid here is a fixed multiple of a unit count, which bounds the units;
+// the bounds are checked before anything is enqueued:
+//   prep: a 256-thread workgroup per (chunk slot, head);
+//   recurrence and fused prefill: 512 work-items per (document, head) unit,
+//     unit counts rounded up to a multiple of 8 (the recurrence takes one
+//     workgroup per unit once the units fill the device);
+//   segment pairs: 1024 per (segment, head); composing them: 2048 per
+//     (segment group, head);
+//   decode and the empty-document copy: a 256-thread workgroup per (sequence, head).
+constexpr int64_t kMaxItems = 0xFFFFFFFFll;
+constexpr int64_t kMaxSlotHeads = kMaxItems / 256;
+constexpr int64_t kMaxDocHeads = kMaxItems / 512 / 8 * 8;
+constexpr int64_t kMaxSegHeads = kMaxItems / 1024 / 8 * 8;
+constexpr int64_t kMaxGroupHeads = kMaxItems / 2048 / 8 * 8;
+constexpr int64_t kMaxSeqHeads = kMaxItems / 256;
 
 // The KDA_RAW_INPUTS flag of a dtype argument; the element type is the rest.
 bool take_raw_flag(int32_t &dtype) {
@@ -56,7 +72,12 @@ int check_layout(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int3
   if (T < 0) return fail(KDA_ERR_SHAPE, "T must be >= 0");
   if (N <= 0) return fail(KDA_ERR_SHAPE, "N must be >= 1 (got %d)", N);
   if (T > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "T must fit int32 offsets");
-  if ((int64_t)N * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "N * H too large");
+  if ((int64_t)N * H > kMaxDocHeads)
+    return fail(KDA_ERR_SHAPE, "N * H = %lld exceeds %lld (one launch)", (long long)N * H,
+                (long long)kMaxDocHeads);
+  if (kda::n_chunk_slots(T, N) * H > kMaxSlotHeads)
+    return fail(KDA_ERR_SHAPE, "chunk slots * H = %lld exceeds %lld (one launch)",
+                (long long)(kda::n_chunk_slots(T, N) * H), (long long)kMaxSlotHeads);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (cu_seqlens) {
     if (!cu_seqlens_host)
@@ -101,8 +122,6 @@ int check_image_workspace(const void *workspace, size_t workspace_bytes, int64_t
   if (!workspace || workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (kda::n_chunk_slots(T, N) * H > (int64_t)INT32_MAX)
-    return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
   return KDA_OK;
 }
 
@@ -508,10 +527,10 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   if (T > 0 && !f32c) {
     // two-kernel path: chunk prep over all chunks, segment pairs and the re-run
     // on the recurrence kernel; segments are ranges of chunk slots
-    const int64_t n_slots = kda::n_chunk_slots(T, N);
-    if (n_slots * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "too many chunks for one launch");
     const SegPlan sp = plan_segments(used_chunk_slots(T, N, cu_seqlens_host), req);
-    if (sp.n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
+    if (sp.n_seg * H > kMaxSegHeads)
+      return fail(KDA_ERR_SHAPE, "segments * H = %lld exceeds %lld (one launch)",
+                  (long long)(sp.n_seg * H), (long long)kMaxSegHeads);
     const size_t need = split_scan_workspace(T, N, H, req);
     if (!workspace || workspace_bytes < need)
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
@@ -519,6 +538,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     // the buffers are laid out for the largest plan the workspace size allows for
     const int64_t n_max = max_split_segments(T, N, req), g_max = max_scan_groups(n_max);
     const int64_t glen = scan_group_len(sp.n_seg), n_groups = scan_groups(sp.n_seg);
+    if (n_groups * H > kMaxGroupHeads)
+      return fail(KDA_ERR_SHAPE, "segment groups * H = %lld exceeds %lld (one launch)",
+                  (long long)(n_groups * H), (long long)kMaxGroupHeads);
     if (sp.n_seg > n_max || n_groups > g_max)
       return fail(KDA_ERR_UNSUPPORTED, "segment plan exceeds its workspace layout (%lld segments, %lld groups)",
                   (long long)sp.n_seg, (long long)n_groups);
@@ -576,7 +598,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
   } else if (T > 0) {
     const SegPlan sp = plan_segments(T, req);
-    if (sp.n_seg * H > (int64_t)INT32_MAX / 8) return fail(KDA_ERR_SHAPE, "too many segments");
+    if (sp.n_seg * H > kMaxSegHeads)
+      return fail(KDA_ERR_SHAPE, "segments * H = %lld exceeds %lld (one launch)",
+                  (long long)(sp.n_seg * H), (long long)kMaxSegHeads);
     const size_t need = scan_workspace(sp.n_seg, H);
     if (!workspace || workspace_bytes < need)
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
@@ -623,7 +647,9 @@ static int decode_common(float *state, int32_t S_pool, const int32_t *state_slot
   if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
     return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");
   if (H > kMaxHeads) return fail(KDA_ERR_SHAPE, "H must be at most %d (got %d)", kMaxHeads, H);
-  if ((int64_t)N * H > (int64_t)INT32_MAX) return fail(KDA_ERR_SHAPE, "N * H too large");
+  if ((int64_t)N * H > kMaxSeqHeads)
+    return fail(KDA_ERR_SHAPE, "N * H = %lld exceeds %lld (one launch)", (long long)N * H,
+                (long long)kMaxSeqHeads);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
   if (!(g_min >= -5.0f && g_min < 0.0f))
     return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);

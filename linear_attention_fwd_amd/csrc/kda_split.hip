@@ -825,7 +825,7 @@ hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
   // the device; the workgroups of one unit share an XCD
   const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
   const int cus = device_cus();
-  const bool wide = cus > 0 && units >= cus;
+  const bool wide = units >= (cus > 0 ? cus : 256);  // the units fill the device
   const int groups = (units + 7) / 8;
   const int nsplit = (p.rmode == 2 ? 4 : 2) / (wide ? 2 : 1);
   const dim3 grid((unsigned)(groups * 8 * nsplit));

@@ -331,6 +331,40 @@ def test_head_count_bound(lib):
                                        None) == KDA_ERR_SHAPE
 
 
+def test_launch_size_bounds(lib):
+    """Sizes whose kernels would exceed one dispatch (2^32 - 1 work-items) are
+    refused before anything is enqueued; the largest accepted sizes pass the
+    shape checks (and then fail on the missing workspace or state instead)."""
+    H = 65535
+    WS = -6  # KDA_ERR_WORKSPACE
+
+    def docs(n):  # n documents of 64 tokens
+        cu = (ctypes.c_int32 * (n + 1))(*range(0, 64 * (n + 1), 64))
+        return dict(N=n, T=64 * n, H=H, cu=FAKE, cu_host=ctypes.cast(cu, ctypes.c_void_p)), cu
+
+    kw, keep = docs(128)   # N * H = 8 388 480, slots * H = 16 776 960
+    assert _prefill(lib, "kda_chunk_fwd", ws=FAKE, **kw) == WS
+    kw, keep = docs(129)   # N * H = 8 454 015
+    assert _prefill(lib, "kda_chunk_fwd", ws=FAKE, **kw) == KDA_ERR_SHAPE
+    assert _prefill(lib, "kda_segment_scan", nseg=4, **kw) == KDA_ERR_SHAPE
+    # chunk slots x heads: floor(T / 64) + N slots
+    assert _prefill(lib, "kda_chunk_fwd", T=64 * 255, H=H, ws=FAKE) == WS           # 256 slots
+    assert _prefill(lib, "kda_chunk_fwd", T=64 * 256, H=H, ws=FAKE) == KDA_ERR_SHAPE  # 257
+    # segment scan: segments x heads <= 4 194 296 (64 segments at H = 65535)
+    for compute in (0, 1):
+        assert _prefill(lib, "kda_segment_scan", T=64 * 65, H=H, nseg=64,
+                        compute=compute) == WS
+        assert _prefill(lib, "kda_segment_scan", T=64 * 65, H=H, nseg=65,
+                        compute=compute) == KDA_ERR_SHAPE
+
+    def dec(N, state):
+        return lib.kda_decode_step(state, N, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, None, -5.0, FAKE, None, N, H, 128, 128,
+                                   1, None)
+    assert dec(256, None) == KDA_ERR_NULL    # N * H = 16 776 960: shape accepted
+    assert dec(257, FAKE) == KDA_ERR_SHAPE   # 16 842 495
+
+
 def test_one_hip_runtime_per_process():
     """Loading the library before torch has touched anything must not bring in a
     second HIP runtime (PyTorch ships its own; with two in one process the one
