@@ -153,6 +153,25 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _out(t, name, shape, dtype):
+    """A caller-supplied output: the library writes through its bare pointer, so
+    it must be a contiguous GPU tensor of exactly this shape and dtype."""
+    if t is None:
+        return None
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ws(t, name="workspace"):
+    """A caller-supplied workspace: a contiguous GPU tensor (its byte size goes to
+    the library, which checks it against what the call needs)."""
+    if t is None or t is False:
+        return t
+    return _dev(t, name)
+
+
 def _seqlens(cu_seqlens, cu_seqlens_host, T, device):
     """Return (device int32 tensor or None, host int32 numpy array or None, N)."""
     torch = _torch()
@@ -210,10 +229,13 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _out(o, "o", (T, H, dv), q.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
     if workspace is None:
         split = _dtype_code(q) == KDA_BF16 and int(compute) == KDA_COMPUTE_AUTO and T > 0
         workspace = (torch.empty(kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
                                  device=q.device) if split else False)
+    _ws(workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is False else \
         (_ptr(workspace), workspace.numel() * workspace.element_size())
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
@@ -246,6 +268,8 @@ def kda_chunk_fwd_noalloc(q, k, v, g_logits, beta, A_log=None, g_min: float = -5
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _out(o, "o", (T, H, dv), q.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
                                    _ptr(A_log), float(g_min), _ptr(initial_state), _ptr(cu_dev),
@@ -271,10 +295,13 @@ def kda_chunk_fwd_unbounded(q, k, v, g_logits, beta, A_log=None, initial_state=N
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _out(o, "o", (T, H, dv), q.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
     if workspace is None:
         workspace = torch.empty(max(1, kda_chunk_fwd_workspace_size(N, T, H, dk, dv)),
                                 dtype=torch.uint8, device=q.device) \
             if _dtype_code(q) == KDA_BF16 else False
+    _ws(workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is False else \
         (_ptr(workspace), workspace.numel() * workspace.element_size())
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
@@ -314,12 +341,16 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _out(o, "o", (T, H, dv), q.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
     if checkpoints is None:
         n = kda_checkpoint_count(N, T, interval)
         checkpoints = torch.empty((max(n, 1), H, dk, dv), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(kda_chunk_fwd_workspace_size(N, T, H, dk, dv), dtype=torch.uint8,
                                 device=q.device)
+    _ws(workspace)
+    _dev(checkpoints, "checkpoints", torch.float32)  # its byte size is checked by the library
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_checkpoints(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log), float(g_min),
@@ -338,6 +369,7 @@ def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -
     lib = load_library()
     T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, q, g_logits, beta, A_log, None,
                                                        cu_seqlens, cu_seqlens_host)
+    _ws(workspace)
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     _check(lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(cu_dev), host_ptr, N, T, H, dk, dv,
@@ -363,6 +395,9 @@ def kda_chunk_recurrence(v, workspace, initial_state=None, cu_seqlens=None, cu_s
         o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+    _out(o, "o", (T, H, dv), v.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    _ws(workspace)
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     _check(lib.kda_chunk_recurrence(_ptr(v), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
                                     dk, dv, _dtype_code(v), _ptr(workspace),
@@ -403,6 +438,9 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _out(o, "o", (T, H, dv), q.dtype)
+    _out(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    _ws(workspace)
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_segment_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
@@ -481,7 +519,7 @@ def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbet
     dt = nq.dtype
     if o is None:
         o = torch.empty((N, H, d), dtype=dt, device=nq.device)
-    _dev(o, "o", dt)
+    _out(o, "o", (N, H, d), dt)
     rc = lib.kda_decode_step(_ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
                              _ptr(cz), _ptr(cbeta), _ptr(accepted), int(W), _ptr(nq), _ptr(nk),
                              _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(A_log), float(g_min), _ptr(o),
@@ -517,8 +555,8 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
         o = torch.empty((N, H, d), dtype=dt, device=nq.device)
     if o_window is None:
         o_window = torch.empty((N, W2, H, d), dtype=dt, device=nq.device)
-    _dev(o_window, "o_window", dt)
-    _dev(o, "o", dt)
+    _out(o_window, "o_window", (N, W2, H, d), dt)
+    _out(o, "o", (N, H, d), dt)
     rc = lib.kda_decode_step_window(
         _ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
         _ptr(accepted), int(W), _ptr(nq), _ptr(nk), _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(wq),
