@@ -152,7 +152,9 @@ size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk,
  * share the scratch and race: order them on one stream.  The scratch's address
  * on a device is looked up by the first call there; make that first call
  * outside any graph capture, after which calls capture and replay like the
- * other entry points (they launch kernels only). */
+ * other entry points (they launch kernels only).  The scratch used is the
+ * current device's, so `stream` must belong to the current device (another
+ * device's stream returns KDA_ERR_UNSUPPORTED). */
 #define KDA_NOALLOC_SCRATCH_BYTES 268435456
 int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_logits,
                           const void *beta, const float *A_log, float g_min,

@@ -312,6 +312,19 @@ int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const voi
                 need, N, (long long)T, H, kda::NOALLOC_SCRATCH_BYTES);
   hipStream_t st = (hipStream_t)stream;
   if (T > 0) {
+    // The scratch is looked up on the current device and the kernels run on
+    // the stream's: a stream of another device would get a foreign address.
+    if (st) {
+      int dev = 0;
+      hipDevice_t sdev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipStreamGetDevice(st, &sdev);
+      if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc stream device");
+      if (sdev != dev)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "kda_chunk_fwd_noalloc: the stream belongs to device %d, not to the current "
+                    "device %d", (int)sdev, dev);
+    }
     void *ws = nullptr;
     hipError_t e = kda::noalloc_scratch(&ws);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc scratch address");

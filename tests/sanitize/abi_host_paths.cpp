@@ -141,6 +141,12 @@ int main() {
   EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
                                KDA_BF16, F, Ff, nullptr),
          KDA_ERR_HIP);
+  EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                               KDA_BF16, F, Ff, (void *)0x1000),
+         KDA_ERR_HIP);  // a stream of the current device
+  EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -5.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                               KDA_BF16, F, Ff, (void *)0x2000),
+         KDA_ERR_UNSUPPORTED);  // a stream of another device
 
   // ---- decode ----
   EXPECT(kda_decode_step(Ff, 7, nullptr, F, F, F, F, F, Fi, 4, F, F, F, F, F, Ff, -5.f, F,

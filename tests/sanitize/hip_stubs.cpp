@@ -19,6 +19,12 @@ hipError_t hipDeviceGetAttribute(int *value, hipDeviceAttribute_t, int) {
   *value = 256;
   return hipSuccess;
 }
+// Streams live on device 0, except the handle 0x2000, which stands for a
+// stream of device 1.
+hipError_t hipStreamGetDevice(hipStream_t stream, hipDevice_t *device) {
+  *device = (uintptr_t)stream == 0x2000 ? 1 : 0;
+  return hipSuccess;
+}
 }
 
 namespace kda {
