@@ -384,6 +384,12 @@ def main():
         q, k, v, z, b, A_log, inp.g_min, o=o, final_state=fin, workspace=ws, raw_inputs=True),
         args.steps, args.warmup)
 
+    # ---------------- the same step on the fused kernel (kda_chunk_fwd without a
+    # workspace: one kernel runs prep and recurrence per chunk, serially)
+    fused_ms, _, _ = timer.run(lambda: kda.kda_chunk_fwd(
+        q, k, v, z, b, A_log, inp.g_min, o=o, final_state=fin, workspace=False),
+        args.steps, args.warmup)
+
     # ---------------- decode with speculative verify -------------------------
     # the decode workload (N=512, H=96, 4 drafts + bonus) plus, drawn after it, a
     # next window of 4 drafts for the fused replay + bonus + window step
@@ -502,6 +508,10 @@ def main():
         "raw_inputs": {"what": "q, k L2-normalised and beta sigmoid in the kernels",
                        "prefill_ms": raw_ms, "prefill_extra_ms": raw_ms - step_ms,
                        "decode_ms": rawd_ms, "decode_extra_ms": rawd_ms - dec_ms},
+        "fused_kernel": {"what": "kda_chunk_fwd without a workspace: prep and recurrence of each "
+                                 "chunk in one workgroup, no chunk images in HBM",
+                         "ms": fused_ms, "extra_ms": fused_ms - step_ms,
+                         "tokens_per_s": T / (fused_ms * 1e-3)},
         "checkpoints": {"interval_tokens": interval, "ms": ck_ms, "extra_ms": ck_ms - step_ms,
                         "state_bytes_written": ck_written},
         "decode": {"workload": "N=512 H=96, 4 drafts + bonus, accepted U{0..4}, fp32 state",
