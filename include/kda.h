@@ -34,6 +34,13 @@
  *     kda_chunk_fwd_noalloc, kda_segment_scan (with the same exception) and
  *     the decode entry points.  kda_chunk_recurrence ignores it (it reads v
  *     only).
+ *   * With KDA_UNBOUNDED_GATE OR'ed into dtype the prefill entry points apply
+ *     the unbounded gate of kda_chunk_fwd_unbounded instead of the bounded one
+ *     (g_min is then not used or checked): kda_chunk_fwd, kda_chunk_fwd_noalloc,
+ *     kda_chunk_fwd_checkpoints, kda_chunk_prep and kda_segment_scan, on every
+ *     arithmetic path.  kda_chunk_recurrence ignores it (the gate is applied in
+ *     the prep); the decode entry points apply the bounded gate only and return
+ *     KDA_ERR_UNSUPPORTED.
  *   * The caller owns every buffer, including workspaces.  The library never
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream).  Return codes describe
@@ -79,6 +86,8 @@ typedef enum kda_status {
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Flag OR'ed into a dtype argument: q, k unnormalised and beta a logit (above). */
 #define KDA_RAW_INPUTS 0x100
+/* Flag OR'ed into a dtype argument: the unbounded gate (above). */
+#define KDA_UNBOUNDED_GATE 0x200
 
 /* Arithmetic of the prefill paths.  KDA_COMPUTE_AUTO picks bf16 MFMA operands
  * with fp32 accumulation for bf16 inputs and fp32 MFMA for fp32 inputs;
@@ -226,11 +235,13 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
  * bounded gate replaces ("Kimi K3 模型结构（2）：序列维度（下）", section
  * "K3 的改动：下界衰减", the Kimi Linear form shared with GDN and Mamba-2):
  *   g = -exp(A_h) * softplus(z),   softplus(z) = log(1 + exp(z)),
- * which has no lower bound.  Without a bound the diagonal 16 x 16 subtiles of
- * the intra-chunk matrices cannot be split into two factors for the matrix
- * cores (same section): they are computed per position pair in fp32, the
- * path whose cost the bounded gate removes; every other step is the one of
- * kda_chunk_fwd.  Arguments as for kda_chunk_fwd without g_min and compute:
+ * which has no lower bound.  Without a bound a diagonal 16 x 16 subtile of the
+ * intra-chunk matrices whose decay range is too wide cannot be split into two
+ * factors for the matrix cores (same section): such subtiles are computed per
+ * position pair in fp32, the path whose cost the bounded gate removes; every
+ * other step is the one of kda_chunk_fwd.  This is kda_chunk_fwd with
+ * KDA_UNBOUNDED_GATE and KDA_COMPUTE_AUTO.  Arguments as for kda_chunk_fwd
+ * without g_min and compute:
  * bf16 inputs with a workspace of kda_chunk_fwd_workspace_size() bytes run the
  * two-kernel path, bf16 inputs with a NULL workspace the fused kernel (both
  * bf16 arithmetic), fp32 inputs the fused kernel in fp32 arithmetic (the

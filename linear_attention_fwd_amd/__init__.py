@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_RAW_INPUTS = 0x100  # OR'ed into dtype: q, k unnormalised and beta a logit
+KDA_UNBOUNDED_GATE = 0x200  # OR'ed into dtype: g = -exp(A) softplus(z) instead of the bounded gate
 KDA_COMPUTE_AUTO, KDA_COMPUTE_F32 = 0, 1
 KDA_DECODE_ERR_ACCEPTED, KDA_DECODE_ERR_SLOT = 1, 2  # bits of a decode step's err_flag
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
@@ -128,11 +129,12 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dtype_code(t, raw_inputs: bool = False) -> int:
+def _dtype_code(t, raw_inputs: bool = False, unbounded_gate: bool = False) -> int:
     """dtype argument of the C ABI for tensor t, with KDA_RAW_INPUTS when q, k are
-    unnormalised and beta is a logit (the kernels normalise and apply the sigmoid)."""
+    unnormalised and beta is a logit (the kernels normalise and apply the sigmoid)
+    and KDA_UNBOUNDED_GATE for the unbounded gate."""
     torch = _torch()
-    flag = KDA_RAW_INPUTS if raw_inputs else 0
+    flag = (KDA_RAW_INPUTS if raw_inputs else 0) | (KDA_UNBOUNDED_GATE if unbounded_gate else 0)
     if t.dtype == torch.bfloat16:
         return KDA_BF16 | flag
     if t.dtype == torch.float32:
@@ -213,13 +215,17 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                   initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                   output_final_state: bool = True, compute: int = KDA_COMPUTE_AUTO,
                   o=None, final_state=None, workspace=None,
-                  raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
+                  raw_inputs: bool = False,
+                  unbounded_gate: bool = False) -> Tuple[object, Optional[object]]:
     """Chunkwise KDA prefill.  q, k, v, g_logits: [T, H, 128]; beta: [T, H] (same
     dtype, bf16 or fp32); A_log: [H] fp32 or None; initial_state: [N, H, 128, 128]
     fp32 or None; cu_seqlens: [N+1] int32 (device and/or host copy).
     workspace: None allocates one (uint8, kda_chunk_fwd_workspace_size bytes) when
     the two-kernel path applies (bf16 inputs, compute AUTO); False runs the fused
     single kernel; a uint8 device tensor is used as given.
+    raw_inputs: q, k unnormalised and beta a logit (normalised and sigmoid in the
+    kernels); unbounded_gate: g = -exp(A_h) softplus(z) instead of the bounded gate
+    (g_min is then unused; the other prefill functions take both flags too).
     Returns (o [T, H, 128] in the input dtype, final_state [N, H, 128, 128] fp32 or None)."""
     torch = _torch()
     lib = load_library()
@@ -241,9 +247,8 @@ def kda_chunk_fwd(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                            float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
-                           dk, dv, _dtype_code(q, raw_inputs), int(compute), _ptr(o),
-                           _ptr(final_state),
-                           ws_ptr, ws_bytes, _stream())
+                           dk, dv, _dtype_code(q, raw_inputs, unbounded_gate), int(compute),
+                           _ptr(o), _ptr(final_state), ws_ptr, ws_bytes, _stream())
     _check(rc)
     return o, final_state
 
@@ -254,7 +259,8 @@ KDA_NOALLOC_SCRATCH_BYTES = 256 << 20  # kda_chunk_fwd_noalloc's device scratch
 def kda_chunk_fwd_noalloc(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                           initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                           output_final_state: bool = True, o=None, final_state=None,
-                          raw_inputs: bool = False) -> Tuple[object, Optional[object]]:
+                          raw_inputs: bool = False,
+                          unbounded_gate: bool = False) -> Tuple[object, Optional[object]]:
     """``kda_chunk_fwd`` (two-kernel path, bf16) whose workspace is the library's
     static device scratch: the C call allocates nothing.  Sizes whose workspace
     exceeds KDA_NOALLOC_SCRATCH_BYTES raise KDAError (KDA_ERR_WORKSPACE).  Pass
@@ -273,7 +279,8 @@ def kda_chunk_fwd_noalloc(q, k, v, g_logits, beta, A_log=None, g_min: float = -5
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta),
                                    _ptr(A_log), float(g_min), _ptr(initial_state), _ptr(cu_dev),
-                                   host_ptr, N, T, H, dk, dv, _dtype_code(q, raw_inputs), _ptr(o),
+                                   host_ptr, N, T, H, dk, dv,
+                                   _dtype_code(q, raw_inputs, unbounded_gate), _ptr(o),
                                    _ptr(final_state), _stream())
     _check(rc)
     return o, final_state
@@ -329,7 +336,7 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
                               g_min: float = -5.0, initial_state=None, cu_seqlens=None,
                               cu_seqlens_host=None, output_final_state: bool = True, o=None,
                               final_state=None, checkpoints=None, workspace=None,
-                              raw_inputs: bool = False):
+                              raw_inputs: bool = False, unbounded_gate: bool = False):
     """kda_chunk_fwd (two-kernel path, bf16) that also writes the state every
     ``interval`` tokens inside each document (see ``checkpoint_index``).
     Returns (o, final_state, checkpoints [kda_checkpoint_count, H, 128, 128] fp32)."""
@@ -354,8 +361,8 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_chunk_fwd_checkpoints(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log), float(g_min),
-        _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H, dk, dv, _dtype_code(q, raw_inputs),
-        int(interval), _ptr(checkpoints), checkpoints.numel() * checkpoints.element_size(),
+        _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H, dk, dv,
+        _dtype_code(q, raw_inputs, unbounded_gate), int(interval), _ptr(checkpoints), checkpoints.numel() * checkpoints.element_size(),
         _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream())
     _check(rc)
@@ -363,7 +370,8 @@ def kda_chunk_fwd_checkpoints(q, k, v, g_logits, beta, interval: int, A_log=None
 
 
 def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -5.0,
-                   cu_seqlens=None, cu_seqlens_host=None, raw_inputs: bool = False) -> None:
+                   cu_seqlens=None, cu_seqlens_host=None, raw_inputs: bool = False,
+                   unbounded_gate: bool = False) -> None:
     """First half of the two-kernel prefill: writes every (head, chunk) image into
     ``workspace`` (uint8, kda_chunk_fwd_workspace_size bytes).  bf16 inputs only."""
     lib = load_library()
@@ -373,7 +381,7 @@ def kda_chunk_prep(q, k, g_logits, beta, workspace, A_log=None, g_min: float = -
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     _check(lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(cu_dev), host_ptr, N, T, H, dk, dv,
-                              _dtype_code(q, raw_inputs), _ptr(workspace),
+                              _dtype_code(q, raw_inputs, unbounded_gate), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream()))
 
 
@@ -422,7 +430,7 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                      initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
                      n_segments: int = 0, output_final_state: bool = True,
                      compute: int = KDA_COMPUTE_AUTO, workspace=None, o=None,
-                     final_state=None, raw_inputs: bool = False):
+                     final_state=None, raw_inputs: bool = False, unbounded_gate: bool = False):
     """Prefill via per-segment affine pairs, an on-device pair scan and a re-run
     from exact entry states.  Same tensors as ``kda_chunk_fwd``; n_segments <= 0
     uses one segment per compute unit.  Returns (o, final_state)."""
@@ -444,7 +452,8 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
     host_ptr = None if cu_host is None else cu_host.ctypes.data_as(ctypes.c_void_p)
     rc = lib.kda_segment_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(g_logits), _ptr(beta), _ptr(A_log),
                               float(g_min), _ptr(initial_state), _ptr(cu_dev), host_ptr, N, T, H,
-                              dk, dv, _dtype_code(q, raw_inputs), int(compute), int(n_seg), _ptr(o),
+                              dk, dv, _dtype_code(q, raw_inputs, unbounded_gate), int(compute),
+                              int(n_seg), _ptr(o),
                               _ptr(final_state), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream())
     _check(rc)

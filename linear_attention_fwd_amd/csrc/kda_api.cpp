@@ -57,6 +57,12 @@ bool take_raw_flag(int32_t &dtype) {
   dtype &= ~KDA_RAW_INPUTS;
   return raw;
 }
+// The KDA_UNBOUNDED_GATE flag of a dtype argument, as the gate map it selects.
+int take_gate_flag(int32_t &dtype) {
+  const bool unb = (dtype & KDA_UNBOUNDED_GATE) != 0;
+  dtype &= ~KDA_UNBOUNDED_GATE;
+  return unb ? kda::GATE_SOFTPLUS : kda::GATE_BOUNDED;
+}
 int raw_unsupported(const char *who) {
   return fail(KDA_ERR_UNSUPPORTED,
               "%s: raw inputs with fp32 arithmetic need fp32 inputs (bf16 inputs would be "
@@ -104,14 +110,14 @@ int check_gate(float g_min) {
 int check_prefill(const void *q, const void *k, const void *v, const void *g_logits,
                   const void *beta, float g_min, const int32_t *cu_seqlens,
                   const int32_t *cu_seqlens_host, int32_t N, int64_t T, int32_t H, int32_t dk,
-                  int32_t dv, int32_t dtype, int32_t compute, const void *o) {
+                  int32_t dv, int32_t dtype, int32_t compute, const void *o, int gate) {
   if (T > 0 && (!q || !k || !v || !g_logits || !beta || !o))
     return fail(KDA_ERR_NULL, "q, k, v, g_logits, beta and o must be non-NULL when T > 0");
   int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
   if (rc != KDA_OK) return rc;
   if (compute != KDA_COMPUTE_AUTO && compute != KDA_COMPUTE_F32)
     return fail(KDA_ERR_DTYPE, "unknown compute mode %d", compute);
-  return check_gate(g_min);
+  return gate == kda::GATE_SOFTPLUS ? KDA_OK : check_gate(g_min);  // the unbounded gate has no g_min
 }
 
 // Workspace of the two-kernel path (chunk images).
@@ -254,8 +260,9 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                   int32_t dk, int32_t dv, int32_t dtype, int32_t compute, void *o,
                   float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
   const bool raw = take_raw_flag(dtype);
+  const int gate = take_gate_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
-                         dk, dv, dtype, compute, o);
+                         dk, dv, dtype, compute, o, gate);
   if (rc != KDA_OK) return rc;
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   const bool split = workspace != nullptr && !f32c;
@@ -270,6 +277,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                                       cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
                                       workspace);
     p.raw = raw;
+    p.gate = gate;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
@@ -281,7 +289,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
     p.mode = 0; p.n_items = N; p.seg_len = 0;
     p.item_init = initial_state; p.doc_init = nullptr;
     p.o = o; p.final_state = final_state;
-    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, f32c, kda::GATE_BOUNDED, raw, st);
+    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, f32c, gate, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd launch");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
@@ -299,8 +307,9 @@ int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const voi
                           void *stream) {
   static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::NOALLOC_SCRATCH_BYTES, "documented limit");
   const bool raw = take_raw_flag(dtype);
+  const int gate = take_gate_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
-                         dk, dv, dtype, KDA_COMPUTE_AUTO, o);
+                         dk, dv, dtype, KDA_COMPUTE_AUTO, o, gate);
   if (rc != KDA_OK) return rc;
   if (dtype != KDA_BF16)
     return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_fwd_noalloc runs the bf16 two-kernel path only");
@@ -331,6 +340,7 @@ int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const voi
     kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, g_min, initial_state,
                                       cu_seqlens, cu_seqlens_host, N, T, H, o, final_state, ws);
     p.raw = raw;
+    p.gate = gate;
     e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_noalloc launch");
@@ -356,8 +366,9 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
                               float *final_state, void *workspace, size_t workspace_bytes,
                               void *stream) {
   const bool raw = take_raw_flag(dtype);
+  const int gate = take_gate_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
-                         dk, dv, dtype, KDA_COMPUTE_AUTO, o);
+                         dk, dv, dtype, KDA_COMPUTE_AUTO, o, gate);
   if (rc != KDA_OK) return rc;
   if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "checkpoints are written by the bf16 two-kernel path only");
   if (interval <= 0 || interval % kC != 0)
@@ -376,6 +387,7 @@ int kda_chunk_fwd_checkpoints(const void *q, const void *k, const void *v, const
     p.ckpt = checkpoints;
     p.ckpt_chunks = interval / kC;
     p.raw = raw;
+    p.gate = gate;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_checkpoints launch");
@@ -393,45 +405,12 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
                             int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *o,
                             float *final_state, void *workspace, size_t workspace_bytes,
                             void *stream) {
-  const float unused_g_min = -5.0f;  // the unbounded gate takes no g_min
-  const bool raw = take_raw_flag(dtype);
-  int rc = check_prefill(q, k, v, g_logits, beta, unused_g_min, cu_seqlens, cu_seqlens_host, N, T,
-                         H, dk, dv, dtype, KDA_COMPUTE_AUTO, o);
-  if (rc != KDA_OK) return rc;
-  // bf16 inputs with a workspace: the two-kernel path; without one: the fused
-  // kernel (bf16 arithmetic); fp32 inputs: the fused kernel in fp32 arithmetic
-  const bool split = dtype == KDA_BF16 && workspace != nullptr;
-  if (split) {
-    rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
-    if (rc != KDA_OK) return rc;
-  }
-  hipStream_t st = (hipStream_t)stream;
-  if (T > 0 && split) {
-    kda::SplitParams p = split_params(q, k, v, g_logits, beta, A_log, unused_g_min, initial_state,
-                                      cu_seqlens, cu_seqlens_host, N, T, H, o, final_state,
-                                      workspace);
-    p.gate = kda::GATE_SOFTPLUS;
-    p.raw = raw;
-    hipError_t e = kda::launch_chunk_prep(p, st);
-    if (e == hipSuccess) e = kda::launch_chunk_recurrence(p, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
-  } else if (T > 0) {
-    kda::FwdParams p{};
-    p.q = q; p.k = k; p.v = v; p.z = g_logits; p.beta = beta;
-    p.A_log = A_log; p.g_min = unused_g_min;
-    p.cu = cu_seqlens; p.N = N; p.T = T; p.H = H;
-    p.mode = 0; p.n_items = N; p.seg_len = 0;
-    p.item_init = initial_state; p.doc_init = nullptr;
-    p.o = o; p.final_state = final_state;
-    hipError_t e = kda::launch_fwd(p, dtype == KDA_BF16, dtype == KDA_F32, kda::GATE_SOFTPLUS,
-                                   raw, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded launch");
-  }
-  if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
-    hipError_t e = kda::launch_copy_empty(cu_seqlens, T, initial_state, final_state, N, H, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_chunk_fwd_unbounded empty documents");
-  }
-  return KDA_OK;
+  // kda_chunk_fwd with the unbounded gate and the arithmetic of the inputs:
+  // bf16 inputs with a workspace take the two kernels, without one the fused
+  // kernel; fp32 inputs take the fused kernel in fp32 arithmetic
+  return kda_chunk_fwd(q, k, v, g_logits, beta, A_log, -5.0f, initial_state, cu_seqlens,
+                       cu_seqlens_host, N, T, H, dk, dv, dtype | KDA_UNBOUNDED_GATE,
+                       KDA_COMPUTE_AUTO, o, final_state, workspace, workspace_bytes, stream);
 }
 
 size_t kda_chunk_fwd_workspace_size(int32_t N, int64_t T, int32_t H, int32_t dk, int32_t dv) {
@@ -445,10 +424,11 @@ int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const voi
                    int32_t dv, int32_t dtype, void *workspace, size_t workspace_bytes,
                    void *stream) {
   const bool raw = take_raw_flag(dtype);
+  const int gate = take_gate_flag(dtype);
   if (T > 0 && (!q || !k || !g_logits || !beta))
     return fail(KDA_ERR_NULL, "q, k, g_logits and beta must be non-NULL when T > 0");
   int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
-  if (rc == KDA_OK) rc = check_gate(g_min);
+  if (rc == KDA_OK && gate == kda::GATE_BOUNDED) rc = check_gate(g_min);
   if (rc != KDA_OK) return rc;
   if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prep takes bf16 inputs only");
   rc = check_image_workspace(workspace, workspace_bytes, T, N, H);
@@ -457,6 +437,7 @@ int kda_chunk_prep(const void *q, const void *k, const void *g_logits, const voi
                                     cu_seqlens, cu_seqlens_host, N, T, H, nullptr, nullptr,
                                     workspace);
   p.raw = raw;
+  p.gate = gate;
   hipError_t e = kda::launch_chunk_prep(p, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : hip_fail(e, "kda_chunk_prep launch");
 }
@@ -466,7 +447,8 @@ int kda_chunk_recurrence(const void *v, const float *initial_state, const int32_
                          int32_t dk, int32_t dv, int32_t dtype, const void *workspace,
                          size_t workspace_bytes, void *o, float *final_state, void *stream) {
   if (T > 0 && (!v || !o)) return fail(KDA_ERR_NULL, "v and o must be non-NULL when T > 0");
-  take_raw_flag(dtype);  // v is never normalised: the flag changes nothing here
+  take_raw_flag(dtype);   // the recurrence reads v and the chunk images only:
+  take_gate_flag(dtype);  // neither flag changes anything here
   int rc = check_layout(cu_seqlens, cu_seqlens_host, N, T, H, dk, dv, dtype);
   if (rc != KDA_OK) return rc;
   if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_recurrence takes bf16 inputs only");
@@ -518,8 +500,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
                      int32_t n_segments, void *o, float *final_state, void *workspace,
                      size_t workspace_bytes, void *stream) {
   const bool raw = take_raw_flag(dtype);
+  const int gate = take_gate_flag(dtype);
   int rc = check_prefill(q, k, v, g_logits, beta, g_min, cu_seqlens, cu_seqlens_host, N, T, H,
-                         dk, dv, dtype, compute, o);
+                         dk, dv, dtype, compute, o, gate);
   if (rc != KDA_OK) return rc;
   if (final_state && initial_state) {
     // [N, H, D, D] fp32 each; any overlap is refused
@@ -569,6 +552,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     p.seg_slots = sp.len;
     p.pairs = pairs;
     p.raw = raw;
+    p.gate = gate;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan prep");
     p.rmode = 2;  // A: segment pairs; resets at document starts are folded into them
@@ -630,7 +614,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     p.doc_init = initial_state;
     // A: segment pairs (M, S~)
     p.mode = 2; p.item_init = nullptr; p.o = nullptr; p.final_state = pairs;
-    hipError_t e = kda::launch_fwd(p, bf16_in, f32c, kda::GATE_BOUNDED, raw, st);
+    hipError_t e = kda::launch_fwd(p, bf16_in, f32c, gate, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
     // B: entry states
     e = kda::launch_pair_scan(pairs, initial_state, cu_seqlens, N, H, (int)sp.n_seg, sp.len,
@@ -638,7 +622,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");
     // C: re-run every segment from its exact entry state
     p.mode = 1; p.item_init = entry; p.o = o; p.final_state = final_state;
-    e = kda::launch_fwd(p, bf16_in, f32c, kda::GATE_BOUNDED, raw, st);
+    e = kda::launch_fwd(p, bf16_in, f32c, gate, raw, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan re-run");
   }
   if (final_state && has_empty_doc(cu_seqlens_host, N, T)) {
@@ -656,6 +640,8 @@ static int decode_common(float *state, int32_t S_pool, const int32_t *state_slot
                          void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
                          int32_t dv, int32_t dtype, void *stream, const char *who) {
   const bool raw = take_raw_flag(dtype);
+  if (take_gate_flag(dtype) != kda::GATE_BOUNDED)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: the decode step applies the bounded gate only", who);
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
   if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
     return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");

@@ -123,7 +123,8 @@ def gpu_chunk_fwd(inp, compute=0, t=None, fused=False):
     t = t or gpu_inputs(inp)
     o, S = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min,
                              t["S0"], t["cu"], t["cu_host"], compute=compute,
-                             workspace=False if fused else None, raw_inputs=inp.raw)
+                             workspace=False if fused else None, raw_inputs=inp.raw,
+                             unbounded_gate=inp.gate == "softplus")
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 
@@ -147,7 +148,8 @@ def gpu_segment_scan(inp, n_segments=0, compute=0, t=None):
     t = t or gpu_inputs(inp)
     o, S = kda.kda_segment_scan(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
                                 inp.g_min, t["S0"], t["cu"], t["cu_host"],
-                                n_segments=n_segments, compute=compute, raw_inputs=inp.raw)
+                                n_segments=n_segments, compute=compute, raw_inputs=inp.raw,
+                                unbounded_gate=inp.gate == "softplus")
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(S)
 

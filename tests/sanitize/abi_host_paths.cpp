@@ -100,6 +100,46 @@ int main() {
   EXPECT(kda_chunk_prep(F, F, F, F, Ff, -5.f, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16, F, ws,
                         nullptr),
          KDA_ERR_HIP);
+  // KDA_UNBOUNDED_GATE: g_min is neither used nor checked (-7 would be refused
+  // by the bounded gate) on every prefill entry point and path; decode refuses it
+  {
+    const int32_t U = KDA_UNBOUNDED_GATE;
+    EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                         KDA_BF16, 0, F, Ff, F, ws, nullptr),
+           KDA_ERR_GATE_BOUND);
+    EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                         KDA_BF16 | U, 0, F, Ff, F, ws, nullptr),
+           KDA_ERR_HIP);  // two kernels
+    EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                         KDA_BF16 | U | KDA_RAW_INPUTS, 0, F, Ff, nullptr, 0, nullptr),
+           KDA_ERR_HIP);  // fused
+    EXPECT(kda_chunk_fwd(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                         KDA_F32 | U, 0, F, Ff, nullptr, 0, nullptr),
+           KDA_ERR_HIP);  // fp32
+    EXPECT(kda_chunk_fwd_noalloc(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                                 KDA_BF16 | U, F, Ff, nullptr),
+           KDA_ERR_HIP);
+    const size_t nck = kda_checkpoint_count(N, T, 128);
+    EXPECT(kda_chunk_fwd_checkpoints(F, F, F, F, F, Ff, -7.f, Ff, Fi, cu.data(), N, T, H, 128, 128,
+                                     KDA_BF16 | U, 128, Ff, nck * H * 128 * 128 * 4, F, Ff, F, ws,
+                                     nullptr),
+           KDA_ERR_HIP);
+    EXPECT(kda_chunk_prep(F, F, F, F, Ff, -7.f, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16 | U, F,
+                          ws, nullptr),
+           KDA_ERR_HIP);
+    EXPECT(kda_chunk_recurrence(F, Ff, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16 | U, F, ws, F,
+                                Ff, nullptr),
+           KDA_ERR_HIP);  // the flag changes nothing here
+    for (int32_t dt : {KDA_BF16, KDA_F32}) {
+      const size_t sws = kda_segment_scan_workspace_size(N, T, H, 7, 128, 128);
+      EXPECT(kda_segment_scan(F, F, F, F, F, Ff, -7.f, nullptr, Fi, cu.data(), N, T, H, 128, 128,
+                              dt | U, 0, 7, F, Ff, F, sws, nullptr),
+             KDA_ERR_HIP);
+    }
+    EXPECT(kda_decode_step(Ff, 8, nullptr, F, F, F, F, F, Fi, 4, F, F, F, F, F, Ff, -5.f, F,
+                           nullptr, 8, H, 128, 128, KDA_BF16 | U, nullptr),
+           KDA_ERR_UNSUPPORTED);
+  }
   EXPECT(kda_chunk_recurrence(F, Ff, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16, F, ws, F, Ff,
                               nullptr),
          KDA_ERR_HIP);

@@ -243,7 +243,7 @@ def test_raw_inputs_flag(lib):
                                  1 << 30 if ws else 0, None)
     assert fwd(1 | RAW, FAKE, compute=1) == KDA_ERR_UNSUPPORTED  # bf16 in, fp32 arithmetic
     assert fwd(1 | RAW, None, compute=1) == KDA_ERR_UNSUPPORTED
-    assert fwd(1 | 0x200, FAKE) == KDA_ERR_DTYPE              # unknown bit
+    assert fwd(1 | 0x400, FAKE) == KDA_ERR_DTYPE              # unknown bit
     for n_seg in (0, 7):  # refused before the device is asked for its compute units
         # (bf16 inputs, fp32 arithmetic)
         assert lib.kda_segment_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, -5.0, None, None, None, 1,
@@ -428,3 +428,18 @@ def test_workspace_size_formula(lib, N, T, H):
     4 bytes per document rounded up to 256; no 32-bit overflow."""
     want = (T // 64 + N) * H * 63488 + (4 * N + 255) // 256 * 256
     assert lib.kda_chunk_fwd_workspace_size(N, T, H, 128, 128) == want
+
+
+def test_unbounded_gate_flag(lib):
+    """KDA_UNBOUNDED_GATE: the prefill entry points neither use nor check g_min
+    under the unbounded gate (-7 would be refused by the bounded one); the
+    decode entry points apply the bounded gate only and refuse the flag.  (The
+    accepted calls would launch kernels; they stop here at the workspace check.)"""
+    G = kda.KDA_UNBOUNDED_GATE
+    assert _prefill(lib, "kda_chunk_fwd", g_min=-7.0, ws=FAKE) == KDA_ERR_GATE_BOUND
+    assert _prefill(lib, "kda_chunk_fwd", g_min=-7.0, ws=FAKE, dtype=1 | G) == KDA_ERR_WORKSPACE
+    assert _prefill(lib, "kda_segment_scan", g_min=-7.0, nseg=4) == KDA_ERR_GATE_BOUND
+    assert _prefill(lib, "kda_segment_scan", g_min=-7.0, nseg=4, dtype=1 | G) == KDA_ERR_WORKSPACE
+    assert lib.kda_decode_step(FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, None, -5.0, FAKE, None, 8, 4, 128, 128, 1 | G,
+                               None) == KDA_ERR_UNSUPPORTED

@@ -532,6 +532,68 @@ def test_unbounded_gate_matches_oracle(name, path):
         assert eo2 <= 1e-3 and es2 <= 1e-3, (eo2, es2)
 
 
+@pytest.mark.parametrize("path", ["chunk_fwd_flag", "segment_scan", "segment_scan_fp32",
+                                  "checkpoints", "noalloc", "prep_recurrence"])
+def test_unbounded_gate_other_entry_points(path):
+    """KDA_UNBOUNDED_GATE on the prefill entry points besides kda_chunk_fwd_unbounded:
+    the segment scan (two kernels, and fp32 inputs through the fused kernel), the
+    checkpoint prefill (checked against the oracle's state after each prefix too),
+    the no-allocation call and the two halves called on their own (both bit for
+    bit equal to kda_chunk_fwd_unbounded), on strong decays with both diagonal
+    forms, documents with initial states and a ragged tail.  g_min is passed as
+    -7, which the bounded gate would refuse: the unbounded gate does not use it."""
+    import dataclasses
+    import torch
+    import linear_attention_fwd_amd as kda
+    from kda_testlib import gpu_inputs, oracle_checkpoints
+    c = dict(UNBOUNDED_CASES["strong_decay_varlen"])
+    seed, T, H = c.pop("seed"), c.pop("T"), c.pop("H")
+    dtype = "f32" if path.endswith("fp32") else "bf16"
+    inp = kda_gen.make_prefill(seed, T, H, dtype, gate="softplus", **c)
+    inp = dataclasses.replace(inp, g_min=-7.0)
+    print(f"[case] unbounded gate via the flag, {path}, T={T} H={H} N={inp.N}", flush=True)
+    t = gpu_inputs(inp)
+    ref = gpu_chunk_fwd_unbounded(dataclasses.replace(inp, g_min=-5.0), t=t)
+    if path == "chunk_fwd_flag":
+        o, S = gpu_chunk_fwd(inp, t=t)
+        assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1])
+    elif path.startswith("segment_scan"):
+        o, S = gpu_segment_scan(inp, n_segments=7, t=t)
+    elif path == "checkpoints":
+        interval = 128
+        o, S, ck = kda.kda_chunk_fwd_checkpoints(t["q"], t["k"], t["v"], t["z"], t["beta"],
+                                                 interval, t["A_log"], inp.g_min, t["S0"], t["cu"],
+                                                 t["cu_host"], unbounded_gate=True)
+        torch.cuda.synchronize()
+        o, S, ck = kda_gen.from_torch(o), kda_gen.from_torch(S), kda_gen.from_torch(ck)
+        assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1])
+        want = oracle_checkpoints(inp, interval)
+        worst = 0.0
+        for (d, j), Sref in want.items():
+            i = kda.checkpoint_index(inp.cu_seqlens, d, j, interval)
+            e, _ = rel_l2_slices(ck[i][None], Sref[None], axis_tokens=False)
+            worst = max(worst, e)
+        print(f"    {len(want)} checkpoints, worst state {worst:.3e}", flush=True)
+        assert worst <= TOL_BF16
+    elif path == "noalloc":
+        o, S = kda.kda_chunk_fwd_noalloc(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"],
+                                         inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                         unbounded_gate=True)
+        torch.cuda.synchronize()
+        o, S = kda_gen.from_torch(o), kda_gen.from_torch(S)
+        assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1])
+    else:
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_size(inp.N, T, H), dtype=torch.uint8,
+                         device="cuda")
+        kda.kda_chunk_prep(t["q"], t["k"], t["z"], t["beta"], ws, t["A_log"], inp.g_min,
+                           t["cu"], t["cu_host"], unbounded_gate=True)
+        o, S = kda.kda_chunk_recurrence(t["v"], ws, t["S0"], t["cu"], t["cu_host"])
+        torch.cuda.synchronize()
+        o, S = kda_gen.from_torch(o), kda_gen.from_torch(S)
+        assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1])
+    _check_prefill(inp, o, S, _tols(inp, 0))
+
+
 # ---------------------------------------------------------------------------
 # raw inputs: q, k normalised and beta = sigmoid(logit) in the kernels
 # ---------------------------------------------------------------------------
