@@ -80,7 +80,7 @@ typedef enum kda_status {
   KDA_ERR_SEQLENS = -5,     /* cu_seqlens not 0-based, not monotone, or not ending at T */
   KDA_ERR_WORKSPACE = -6,   /* workspace NULL, misaligned or smaller than required */
   KDA_ERR_HIP = -7,         /* a HIP launch failed (see kda_last_error) */
-  KDA_ERR_UNSUPPORTED = -8  /* valid request this build does not implement */
+  KDA_ERR_UNSUPPORTED = -8  /* a valid request the library does not implement */
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
