@@ -232,6 +232,7 @@ class DecodeInputs:
     wbeta: Optional[Tensor] = None  # [N, W2, H]
     W2: int = 0
     raw: bool = False     # q, k unnormalised and beta a logit (normalised in the operator)
+    gate: str = "bounded"  # "bounded" (g_min applies) or "softplus" (no lower bound)
 
     @property
     def N(self) -> int:
@@ -244,11 +245,13 @@ class DecodeInputs:
 
 def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
                 A_std: float = 0.5, s_std: float = 0.02, d: int = D,
-                accepted=None, W2: int = 0, raw: bool = False) -> DecodeInputs:
+                accepted=None, W2: int = 0, raw: bool = False,
+                gate: str = "bounded") -> DecodeInputs:
     """Decode-with-verify recipe: draft cache first (q,k,v,z,beta order), then A,
     the saved state, the accepted lengths U{0..W}, then the bonus token, then (if
     W2 > 0) the W2 drafts of the next window.  The draws of a call with W2 > 0
-    start with exactly those of the same call with W2 = 0."""
+    start with exactly those of the same call with W2 = 0.  ``gate`` names the
+    gate the operator applies ("bounded" or "softplus"); it changes no draw."""
     rng = np.random.default_rng(seed)
     T = N * W
     q, k, v, z, beta = _draw_qkvzb(rng, T, H, d, dtype, raw=raw)
@@ -276,7 +279,7 @@ def make_decode(seed: int, N: int, H: int, W: int = 4, dtype: str = "bf16", *,
                    wbeta=Tensor(wb.data.reshape(N, W2, H), dtype), W2=W2)
     return DecodeInputs(state=state, cq=cq, ck=ck, cv=cv, cz=cz, cbeta=cb, accepted=acc,
                         nq=nq, nk=nk, nv=nv, nz=nz, nbeta=nb, A_log=A_log, W=W, dtype=dtype,
-                        raw=raw, **win)
+                        raw=raw, gate=gate, **win)
 
 
 # ----------------------------------------------------------------------------

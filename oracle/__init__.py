@@ -205,7 +205,7 @@ def decode(inp, nthreads: int = 0):
         q[s:s + a], k[s:s + a], v[s:s + a], z[s:s + a], b[s:s + a] = (
             cq[n, :a], ck[n, :a], cv[n, :a], cz[n, :a], cb[n, :a])
         q[s + a], k[s + a], v[s + a], z[s + a], b[s + a] = nq[n], nk[n], nv[n], nz[n], nb[n]
-    g = gate(z, inp.A_log, inp.g_min)
+    g = gate_of(inp, z)
     q, k, b = operands(inp, q, k, b)
     o, S = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
     o_bonus = o[cu[1:] - 1]
@@ -241,7 +241,7 @@ def decode_window(inp, nthreads: int = 0):
             q[s:s + m], k[s:s + m], v[s:s + m], z[s:s + m], b[s:s + m] = (
                 pq[n, :m], pk[n, :m], pv[n, :m], pz[n, :m], pb[n, :m])
             s += m
-    g = gate(z, inp.A_log, inp.g_min)
+    g = gate_of(inp, z)
     q, k, b = operands(inp, q, k, b)
     o, _ = recurrent(q, k, v, g, b, inp.state.astype(np.float64), cu, nthreads)
     o_bonus = o[cu[:-1] + acc]

@@ -282,14 +282,17 @@ def test_packed_documents_are_independent(oracle_mod):
     assert np.array_equal(S[1], S0[1])
 
 
-def test_decode_replay_equals_explicit_steps(oracle_mod):
+@pytest.mark.parametrize("gate", ["bounded", "softplus"])
+def test_decode_replay_equals_explicit_steps(oracle_mod, gate):
     """Replay of the accepted drafts plus the bonus token (systems page, decode)
     from the saved state equals eq. (1) stepped explicitly over the same tokens;
     the rejected drafts leave no trace (no rollback needed)."""
     inp = kda_gen.make_decode(11, N=6, H=2, W=4, dtype="bf16", d=128,
-                              accepted=[0, 1, 2, 3, 4, 2])
+                              accepted=[0, 1, 2, 3, 4, 2], gate=gate)
     o, S = oracle_mod.decode(inp)
-    gate = lambda z: oracle_mod.gate(z[None, None, :], inp.A_log[None, h:h + 1], inp.g_min)[0, 0]
+    gfun = oracle_mod.gate_softplus if gate == "softplus" else \
+        (lambda z, A: oracle_mod.gate(z, A, inp.g_min))
+    gate_h = lambda z: gfun(z[None, None, :], inp.A_log[None, h:h + 1])[0, 0]
     for n in range(inp.N):
         a = int(inp.accepted[n])
         for h in range(inp.H):
@@ -298,22 +301,25 @@ def test_decode_replay_equals_explicit_steps(oracle_mod):
             vs = np.concatenate([inp.cv.f64()[n, :a, h], inp.nv.f64()[n, None, h]])
             zs = np.concatenate([inp.cz.f64()[n, :a, h], inp.nz.f64()[n, None, h]])
             bs = np.concatenate([inp.cbeta.f64()[n, :a, h], inp.nbeta.f64()[n, None, h]])
-            gs = np.stack([gate(z) for z in zs])
+            gs = np.stack([gate_h(z) for z in zs])
             ob, Sb = brute.run(qs, ks, vs, gs, bs, inp.state[n, h].astype(np.float64))
             assert _rel(o[n, h], ob[-1]) < 1e-12
             assert _rel(S[n, h], Sb) < 1e-12
 
 
-def test_decode_window_equals_explicit_steps(oracle_mod):
+@pytest.mark.parametrize("gate", ["bounded", "softplus"])
+def test_decode_window_equals_explicit_steps(oracle_mod, gate):
     """Replay, bonus token and the next draft window in one loop (systems page,
     decode): the window drafts' outputs are eq. (1) stepped explicitly past the
     bonus token, and the state kept is the one after the bonus token, whatever
     the window holds."""
     inp = kda_gen.make_decode(12, N=5, H=2, W=4, dtype="bf16", d=128,
-                              accepted=[0, 4, 1, 3, 2], W2=3)
+                              accepted=[0, 4, 1, 3, 2], W2=3, gate=gate)
     o, ow, S = oracle_mod.decode_window(inp)
     assert ow.shape == (inp.N, 3, inp.H, 128)
-    gate = lambda z: oracle_mod.gate(z[None, None, :], inp.A_log[None, h:h + 1], inp.g_min)[0, 0]
+    gfun = oracle_mod.gate_softplus if gate == "softplus" else \
+        (lambda z, A: oracle_mod.gate(z, A, inp.g_min))
+    gate_h = lambda z: gfun(z[None, None, :], inp.A_log[None, h:h + 1])[0, 0]
     cat = lambda c, b, w, n, a, h: np.concatenate([c.f64()[n, :a, h], b.f64()[n, None, h],
                                                     w.f64()[n, :, h]])
     for n in range(inp.N):
@@ -324,7 +330,7 @@ def test_decode_window_equals_explicit_steps(oracle_mod):
             vs = cat(inp.cv, inp.nv, inp.wv, n, a, h)
             zs = cat(inp.cz, inp.nz, inp.wz, n, a, h)
             bs = cat(inp.cbeta, inp.nbeta, inp.wbeta, n, a, h)
-            gs = np.stack([gate(z) for z in zs])
+            gs = np.stack([gate_h(z) for z in zs])
             S0 = inp.state[n, h].astype(np.float64)
             ob, _ = brute.run(qs, ks, vs, gs, bs, S0)
             _, Sb = brute.run(qs[:a + 1], ks[:a + 1], vs[:a + 1], gs[:a + 1], bs[:a + 1], S0)
