@@ -78,8 +78,10 @@ PIN_TESTS = [
     lambda m: pins.test_matches_explicit_transition_matrices(m, 16),
     lambda m: pins.test_chunk_form_equals_recurrence(m, 16, 200),
     pins.test_segment_pairs_compose_to_serial_state,
-    pins.test_decode_replay_equals_explicit_steps,
-    pins.test_decode_window_equals_explicit_steps,
+    lambda m: pins.test_decode_replay_equals_explicit_steps(m, "bounded"),
+    lambda m: pins.test_decode_replay_equals_explicit_steps(m, "softplus"),
+    lambda m: pins.test_decode_window_equals_explicit_steps(m, "bounded"),
+    lambda m: pins.test_decode_window_equals_explicit_steps(m, "softplus"),
 ]
 
 
