@@ -34,13 +34,13 @@
  *     kda_chunk_fwd_noalloc, kda_segment_scan (with the same exception) and
  *     the decode entry points.  kda_chunk_recurrence ignores it (it reads v
  *     only).
- *   * With KDA_UNBOUNDED_GATE OR'ed into dtype the prefill entry points apply
- *     the unbounded gate of kda_chunk_fwd_unbounded instead of the bounded one
+ *   * With KDA_UNBOUNDED_GATE OR'ed into dtype the entry points apply the
+ *     unbounded gate of kda_chunk_fwd_unbounded instead of the bounded one
  *     (g_min is then not used or checked): kda_chunk_fwd, kda_chunk_fwd_noalloc,
- *     kda_chunk_fwd_checkpoints, kda_chunk_prep and kda_segment_scan, on every
- *     arithmetic path.  kda_chunk_recurrence ignores it (the gate is applied in
- *     the prep); the decode entry points apply the bounded gate only and return
- *     KDA_ERR_UNSUPPORTED.
+ *     kda_chunk_fwd_checkpoints, kda_chunk_prep and kda_segment_scan on every
+ *     arithmetic path, and the decode entry points, so that a model with this
+ *     gate decodes with the gate it prefilled with.  kda_chunk_recurrence
+ *     ignores it (the gate is applied in the prep).
  *   * The caller owns every buffer, including workspaces.  The library never
  *     allocates, frees or synchronises; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream).  Return codes describe

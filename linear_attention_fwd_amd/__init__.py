@@ -513,7 +513,7 @@ def _decode_common(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta
 
 def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
                     A_log=None, g_min: float = -5.0, state_slots=None, o=None, err_flag=None,
-                    raw_inputs: bool = False):
+                    raw_inputs: bool = False, unbounded_gate: bool = False):
     """One decode step with speculative-verify replay, updating ``state`` in place.
 
     state: [S_pool, H, 128, 128] fp32; cq, ck, cv, cz: [N, W, H, 128]; cbeta: [N, W, H];
@@ -532,7 +532,8 @@ def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbet
     rc = lib.kda_decode_step(_ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv),
                              _ptr(cz), _ptr(cbeta), _ptr(accepted), int(W), _ptr(nq), _ptr(nk),
                              _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(A_log), float(g_min), _ptr(o),
-                             _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())
+                             _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs, unbounded_gate),
+                             _stream())
     _check(rc)
     return o
 
@@ -540,7 +541,7 @@ def kda_decode_step(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbet
 def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, nz, nbeta,
                            wq, wk, wv, wz, wbeta, A_log=None, g_min: float = -5.0,
                            state_slots=None, o=None, o_window=None, err_flag=None,
-                           raw_inputs: bool = False):
+                           raw_inputs: bool = False, unbounded_gate: bool = False):
     """``kda_decode_step`` followed, in the same kernel, by the next draft window.
 
     Arguments as for ``kda_decode_step`` plus wq, wk, wv, wz: [N, W2, H, 128] and
@@ -570,7 +571,8 @@ def kda_decode_step_window(state, cq, ck, cv, cz, cbeta, accepted, nq, nk, nv, n
         _ptr(state), S_pool, _ptr(state_slots), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(cz), _ptr(cbeta),
         _ptr(accepted), int(W), _ptr(nq), _ptr(nk), _ptr(nv), _ptr(nz), _ptr(nbeta), _ptr(wq),
         _ptr(wk), _ptr(wv), _ptr(wz), _ptr(wbeta), int(W2), _ptr(A_log), float(g_min), _ptr(o),
-        _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs), _stream())
+        _ptr(o_window), _ptr(err_flag), N, H, d, d, _dtype_code(nq, raw_inputs, unbounded_gate),
+        _stream())
     _check(rc)
     return o, o_window
 

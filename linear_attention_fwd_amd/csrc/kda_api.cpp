@@ -640,8 +640,7 @@ static int decode_common(float *state, int32_t S_pool, const int32_t *state_slot
                          void *o, int32_t *err_flag, int32_t N, int32_t H, int32_t dk,
                          int32_t dv, int32_t dtype, void *stream, const char *who) {
   const bool raw = take_raw_flag(dtype);
-  if (take_gate_flag(dtype) != kda::GATE_BOUNDED)
-    return fail(KDA_ERR_UNSUPPORTED, "%s: the decode step applies the bounded gate only", who);
+  const int gate = take_gate_flag(dtype);
   if (dk != kD || dv != kD) return fail(KDA_ERR_SHAPE, "only d_k = d_v = 128 is supported");
   if (N < 0 || H <= 0 || W < 0 || win.W2 < 0)
     return fail(KDA_ERR_SHAPE, "need N >= 0, H > 0, W >= 0, W2 >= 0");
@@ -650,7 +649,7 @@ static int decode_common(float *state, int32_t S_pool, const int32_t *state_slot
     return fail(KDA_ERR_SHAPE, "N * H = %lld exceeds %lld (one launch)", (long long)N * H,
                 (long long)kMaxSeqHeads);
   if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
-  if (!(g_min >= -5.0f && g_min < 0.0f))
+  if (gate == kda::GATE_BOUNDED && !(g_min >= -5.0f && g_min < 0.0f))
     return fail(KDA_ERR_GATE_BOUND, "g_min must lie in [-5, 0) (got %g)", (double)g_min);
   if (S_pool < 0) return fail(KDA_ERR_SHAPE, "S_pool must be >= 0 (got %d)", S_pool);
   if (!state_slots && S_pool < N)
@@ -666,11 +665,11 @@ static int decode_common(float *state, int32_t S_pool, const int32_t *state_slot
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = (dtype == KDA_BF16)
       ? kda::launch_decode<kda::bf16_t>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq,
-                                        nk, nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N,
-                                        H, S_pool, st)
+                                        nk, nv, nz, nbeta, win, raw, A_log, g_min, gate, o,
+                                        err_flag, N, H, S_pool, st)
       : kda::launch_decode<float>(state, state_slots, cq, ck, cv, cz, cbeta, accepted, W, nq, nk,
-                                  nv, nz, nbeta, win, raw, A_log, g_min, o, err_flag, N, H,
-                                  S_pool, st);
+                                  nv, nz, nbeta, win, raw, A_log, g_min, gate, o, err_flag, N,
+                                  H, S_pool, st);
   if (e != hipSuccess) return hip_fail(e, who);
   return KDA_OK;
 }

@@ -48,7 +48,7 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
                   const Tin *__restrict__ nq, const Tin *__restrict__ nk,
                   const Tin *__restrict__ nv, const Tin *__restrict__ nz,
                   const Tin *__restrict__ nbeta, DecodeWindow<Tin> win,
-                  const float *__restrict__ A_log, float g_min, Tin *__restrict__ o,
+                  const float *__restrict__ A_log, float g_min, int gate, Tin *__restrict__ o,
                   int32_t *__restrict__ err_flag, int H, int S_pool) {
   __shared__ __align__(16) float s_k[DEC_TOKBATCH][D];
   __shared__ float s_qsc[DEC_TOKBATCH], s_ksc[DEC_TOKBATCH];  // raw inputs: 1 / ||q||, 1 / ||k||
@@ -114,6 +114,7 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
   }
 
   const float escale = __expf(A_log ? A_log[h] : 0.0f);
+  const float c1s = -escale * 1.4426950408889634f;  // unbounded gate, base 2
 
   for (int t0 = 0; t0 < ntok; t0 += DEC_TOKBATCH) {
     const int nb = min(DEC_TOKBATCH, ntok - t0);
@@ -135,7 +136,9 @@ kda_decode_kernel(float *__restrict__ state, const int32_t *__restrict__ slots,
       s_q[tt][c] = io<Tin>::load1(pq + c);
       s_k[tt][c] = io<Tin>::load1(pk + c);
       s_v[tt][c] = io<Tin>::load1(pv + c);
-      s_a[tt][c] = __expf(kda_gate(io<Tin>::load1(pz + c), escale, g_min));
+      const float zc = io<Tin>::load1(pz + c);
+      s_a[tt][c] = gate == GATE_SOFTPLUS ? __builtin_amdgcn_exp2f(kda_gate2_softplus(zc, c1s))
+                                         : __expf(kda_gate(zc, escale, g_min));
     }
     if (tid < nb) {
       const int t = t0 + tid;
@@ -302,7 +305,7 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const int32_t *accepted, int W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
                          const DecodeWindowArgs &w, bool raw, const float *A_log, float g_min,
-                         void *o, int32_t *err_flag, int N, int H, int S_pool,
+                         int gate, void *o, int32_t *err_flag, int N, int H, int S_pool,
                          hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)N * H));
   DecodeWindow<Tin> win{w.W2, (const Tin *)w.q, (const Tin *)w.k, (const Tin *)w.v,
@@ -311,8 +314,8 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
   hipLaunchKernelGGL(kernel, grid, dim3(DEC_THREADS), 0, stream, state, slots, (const Tin *)cq,
                      (const Tin *)ck, (const Tin *)cv, (const Tin *)cz, (const Tin *)cbeta,
                      accepted, W, (const Tin *)nq, (const Tin *)nk, (const Tin *)nv,
-                     (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min, (Tin *)o, err_flag, H,
-                     S_pool);
+                     (const Tin *)nz, (const Tin *)nbeta, win, A_log, g_min, gate, (Tin *)o, err_flag,
+                     H, S_pool);
   return hipGetLastError();
 }
 
@@ -321,12 +324,12 @@ template hipError_t launch_decode<float>(float *, const int32_t *, const void *,
                                          const int32_t *, int, const void *, const void *,
                                          const void *, const void *, const void *,
                                          const DecodeWindowArgs &, bool, const float *, float,
-                                         void *, int32_t *, int, int, int, hipStream_t);
+                                         int, void *, int32_t *, int, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(float *, const int32_t *, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const int32_t *, int, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const DecodeWindowArgs &, bool, const float *, float,
-                                          void *, int32_t *, int, int, int, hipStream_t);
+                                          int, void *, int32_t *, int, int, int, hipStream_t);
 
 }  // namespace kda

@@ -143,7 +143,7 @@ hipError_t launch_decode(float *state, const int32_t *slots, const void *cq, con
                          const int32_t *accepted, int W, const void *nq, const void *nk,
                          const void *nv, const void *nz, const void *nbeta,
                          const DecodeWindowArgs &win, bool raw, const float *A_log,
-                         float g_min, void *o, int32_t *err_flag, int N, int H,
+                         float g_min, int gate, void *o, int32_t *err_flag, int N, int H,
                          int S_pool, hipStream_t stream);
 
 }  // namespace kda

@@ -174,7 +174,7 @@ def gpu_decode(inp, t=None, state_slots=None, err_flag=None):
     o = kda.kda_decode_step(t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"],
                             t["accepted"], t["nq"], t["nk"], t["nv"], t["nz"], t["nbeta"],
                             t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag,
-                            raw_inputs=inp.raw)
+                            raw_inputs=inp.raw, unbounded_gate=inp.gate == "softplus")
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(t["state"])
 
@@ -187,7 +187,8 @@ def gpu_decode_window(inp, t=None, state_slots=None, err_flag=None):
     o, ow = kda.kda_decode_step_window(
         t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"], t["accepted"], t["nq"],
         t["nk"], t["nv"], t["nz"], t["nbeta"], t["wq"], t["wk"], t["wv"], t["wz"], t["wbeta"],
-        t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag, raw_inputs=inp.raw)
+        t["A_log"], inp.g_min, state_slots=state_slots, err_flag=err_flag, raw_inputs=inp.raw,
+        unbounded_gate=inp.gate == "softplus")
     torch.cuda.synchronize()
     return kda_gen.from_torch(o), kda_gen.from_torch(ow), kda_gen.from_torch(t["state"])
 

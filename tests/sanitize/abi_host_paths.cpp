@@ -136,9 +136,9 @@ int main() {
                               dt | U, 0, 7, F, Ff, F, sws, nullptr),
              KDA_ERR_HIP);
     }
-    EXPECT(kda_decode_step(Ff, 8, nullptr, F, F, F, F, F, Fi, 4, F, F, F, F, F, Ff, -5.f, F,
+    EXPECT(kda_decode_step(Ff, 8, nullptr, F, F, F, F, F, Fi, 4, F, F, F, F, F, Ff, -7.f, F,
                            nullptr, 8, H, 128, 128, KDA_BF16 | U, nullptr),
-           KDA_ERR_UNSUPPORTED);
+           KDA_ERR_HIP);
   }
   EXPECT(kda_chunk_recurrence(F, Ff, Fi, cu.data(), N, T, H, 128, 128, KDA_BF16, F, ws, F, Ff,
                               nullptr),

@@ -49,8 +49,8 @@ template <typename Tin>
 hipError_t launch_decode(float *, const int32_t *, const void *, const void *, const void *,
                          const void *, const void *, const int32_t *, int, const void *,
                          const void *, const void *, const void *, const void *,
-                         const DecodeWindowArgs &, bool, const float *, float, void *, int32_t *,
-                         int, int, int, hipStream_t) {
+                         const DecodeWindowArgs &, bool, const float *, float, int, void *,
+                         int32_t *, int, int, int, hipStream_t) {
   return launched();
 }
 template hipError_t launch_decode<float>(float *, const int32_t *, const void *, const void *,
@@ -58,11 +58,11 @@ template hipError_t launch_decode<float>(float *, const int32_t *, const void *,
                                          const int32_t *, int, const void *, const void *,
                                          const void *, const void *, const void *,
                                          const DecodeWindowArgs &, bool, const float *, float,
-                                         void *, int32_t *, int, int, int, hipStream_t);
+                                         int, void *, int32_t *, int, int, int, hipStream_t);
 template hipError_t launch_decode<bf16_t>(float *, const int32_t *, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const int32_t *, int, const void *, const void *,
                                           const void *, const void *, const void *,
                                           const DecodeWindowArgs &, bool, const float *, float,
-                                          void *, int32_t *, int, int, int, hipStream_t);
+                                          int, void *, int32_t *, int, int, int, hipStream_t);
 }  // namespace kda

@@ -431,15 +431,18 @@ def test_workspace_size_formula(lib, N, T, H):
 
 
 def test_unbounded_gate_flag(lib):
-    """KDA_UNBOUNDED_GATE: the prefill entry points neither use nor check g_min
-    under the unbounded gate (-7 would be refused by the bounded one); the
-    decode entry points apply the bounded gate only and refuse the flag.  (The
-    accepted calls would launch kernels; they stop here at the workspace check.)"""
+    """KDA_UNBOUNDED_GATE: the entry points neither use nor check g_min under the
+    unbounded gate (-7 would be refused by the bounded one).  (The accepted calls
+    would launch kernels; they stop here at a later check: the workspace, or the
+    missing decode state.)"""
     G = kda.KDA_UNBOUNDED_GATE
     assert _prefill(lib, "kda_chunk_fwd", g_min=-7.0, ws=FAKE) == KDA_ERR_GATE_BOUND
     assert _prefill(lib, "kda_chunk_fwd", g_min=-7.0, ws=FAKE, dtype=1 | G) == KDA_ERR_WORKSPACE
     assert _prefill(lib, "kda_segment_scan", g_min=-7.0, nseg=4) == KDA_ERR_GATE_BOUND
     assert _prefill(lib, "kda_segment_scan", g_min=-7.0, nseg=4, dtype=1 | G) == KDA_ERR_WORKSPACE
-    assert lib.kda_decode_step(FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
-                               FAKE, FAKE, FAKE, None, -5.0, FAKE, None, 8, 4, 128, 128, 1 | G,
-                               None) == KDA_ERR_UNSUPPORTED
+    def dec(dtype, state):
+        return lib.kda_decode_step(state, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, None, -7.0, FAKE, None, 8, 4, 128, 128,
+                                   dtype, None)
+    assert dec(1, FAKE) == KDA_ERR_GATE_BOUND
+    assert dec(1 | G, None) == KDA_ERR_NULL

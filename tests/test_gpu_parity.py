@@ -652,11 +652,14 @@ def test_raw_inputs_decode_window(dtype):
 # ---------------------------------------------------------------------------
 # decode with speculative-verify replay
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gate", ["bounded", "softplus"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_matches_oracle(dtype):
+def test_decode_matches_oracle(dtype, gate):
+    """Replay + bonus from the saved state; with gate="softplus" the unbounded gate
+    (KDA_UNBOUNDED_GATE) that a model prefilled with it decodes with."""
     inp = kda_gen.make_decode(51, N=40, H=4, W=4, dtype=dtype,
-                              accepted=[i % 5 for i in range(40)])
-    print(f"[case] decode N={inp.N} H={inp.H} W={inp.W} dtype={dtype}", flush=True)
+                              accepted=[i % 5 for i in range(40)], gate=gate)
+    print(f"[case] decode N={inp.N} H={inp.H} W={inp.W} dtype={dtype} gate={gate}", flush=True)
     o_ref, S_ref = oracle.decode(inp)
     o, S = gpu_decode(inp)
     eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
@@ -728,9 +731,11 @@ def test_decode_skips_slots_outside_the_pool(W2):
     assert np.all(P[untouched] == 3.0)
 
 
-@pytest.mark.parametrize("dtype,W2", [("bf16", 4), ("f32", 4), ("bf16", 13), ("f32", 1),
-                                      ("f32", 7)])
-def test_decode_window_matches_oracle(dtype, W2):
+@pytest.mark.parametrize("dtype,W2,gate", [("bf16", 4, "bounded"), ("f32", 4, "bounded"),
+                                           ("bf16", 13, "bounded"), ("f32", 1, "bounded"),
+                                           ("f32", 7, "bounded"), ("bf16", 4, "softplus"),
+                                           ("f32", 7, "softplus")])
+def test_decode_window_matches_oracle(dtype, W2, gate):
     """Replay + bonus + next draft window in one kernel: the bonus output and the
     state kept equal those of kda_decode_step bit for bit (the same arithmetic on
     the same tokens), and the window drafts' outputs match the oracle.  The last
@@ -739,9 +744,9 @@ def test_decode_window_matches_oracle(dtype, W2):
     on the accepted length, W2 = 13 runs the token loop past two batches."""
     import torch
     inp = kda_gen.make_decode(54, N=24, H=4, W=4, dtype=dtype,
-                              accepted=[i % 5 for i in range(24)], W2=W2)
-    print(f"[case] decode window N={inp.N} H={inp.H} W={inp.W} W2={W2} dtype={dtype}",
-          flush=True)
+                              accepted=[i % 5 for i in range(24)], W2=W2, gate=gate)
+    print(f"[case] decode window N={inp.N} H={inp.H} W={inp.W} W2={W2} dtype={dtype} "
+          f"gate={gate}", flush=True)
     o_ref, ow_ref, S_ref = oracle.decode_window(inp)
     o, ow, S = gpu_decode_window(inp)
     o1, S1 = gpu_decode(inp)
