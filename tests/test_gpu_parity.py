@@ -671,6 +671,32 @@ def test_decode_matches_oracle(dtype, gate):
     assert eo <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_long_draft_cache(dtype):
+    """A draft cache of W = 12: replays of up to 13 tokens span two staging
+    batches of 8, so the bonus token and the state kept fall in the second batch
+    for some sequences and in the first for others; a next window of 3 drafts
+    follows on either side of that boundary."""
+    accepted = [0, 1, 5, 6, 7, 8, 9, 11, 12, 12, 3, 10]
+    inp = kda_gen.make_decode(57, N=len(accepted), H=3, W=12, dtype=dtype, accepted=accepted,
+                              W2=3)
+    print(f"[case] decode long cache N={inp.N} H={inp.H} W={inp.W} W2=3 dtype={dtype}",
+          flush=True)
+    o_ref, S_ref = oracle.decode(inp)
+    _, ow_ref, _ = oracle.decode_window(inp)
+    o, S = gpu_decode(inp)
+    o2, ow, S2 = gpu_decode_window(inp)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    eo, _ = rel_l2_slices(o[:, :, None], o_ref[:, :, None], axis_tokens=False)
+    es, _ = rel_l2_slices(S, S_ref, axis_tokens=False)
+    ew = max(rel_l2_slices(ow[:, j][:, :, None], ow_ref[:, j][:, :, None], axis_tokens=False)[0]
+             for j in range(3))
+    print(f"    o: {eo:.3e}  window: {ew:.3e}  state: {es:.3e}", flush=True)
+    assert es <= TOL_F32
+    assert eo <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    assert ew <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
 def test_decode_slots_and_clamping():
     import torch
     inp = kda_gen.make_decode(52, N=6, H=2, W=4, dtype="bf16", accepted=[0, 4, 7, -1, 2, 3])
