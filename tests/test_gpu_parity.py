@@ -188,6 +188,47 @@ def test_chunk_fwd_is_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+@pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32", "checkpoints", "noalloc",
+                                  "segment_scan", "segment_scan_fp32"])
+def test_prefill_without_final_state(path):
+    """final_state = NULL (output_final_state=False) on every prefill path: O is
+    the same bit for bit as with the final states written, nothing is written in
+    their place (the documents include empty ones, whose final state would
+    otherwise be a copy of the initial one)."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    from kda_testlib import gpu_inputs
+    inp = kda_gen.make_prefill(37, 700, 3, "bf16", lengths=[130, 0, 257, 1, 0, 312],
+                               s0_std=0.05, s0_docs="all")
+    _case(inp, 1 if path.endswith("fp32") else 0)
+    print(f"    path {path}", flush=True)
+    t = gpu_inputs(inp)
+    args = (t["q"], t["k"], t["v"], t["z"], t["beta"])
+    compute = 1 if path.endswith("fp32") else 0
+
+    def run(keep):
+        if path == "checkpoints":
+            return kda.kda_chunk_fwd_checkpoints(*args, 128, t["A_log"], inp.g_min, t["S0"],
+                                                 t["cu"], t["cu_host"],
+                                                 output_final_state=keep)[:2]
+        if path == "noalloc":
+            return kda.kda_chunk_fwd_noalloc(*args, t["A_log"], inp.g_min, t["S0"], t["cu"],
+                                             t["cu_host"], output_final_state=keep)
+        if path.startswith("segment_scan"):
+            return kda.kda_segment_scan(*args, t["A_log"], inp.g_min, t["S0"], t["cu"],
+                                        t["cu_host"], n_segments=5, output_final_state=keep,
+                                        compute=compute)
+        return kda.kda_chunk_fwd(*args, t["A_log"], inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                 output_final_state=keep, compute=compute,
+                                 workspace=False if path == "fused" else None)
+
+    o_ref, S_ref = run(True)
+    o, S = run(False)
+    torch.cuda.synchronize()
+    assert S is None and S_ref is not None
+    assert np.array_equal(kda_gen.from_torch(o), kda_gen.from_torch(o_ref))
+
+
 @pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32", "unbounded", "checkpoints"])
 def test_final_state_in_place(path):
     """kda_chunk_fwd and its variants may write the final states over the initial
