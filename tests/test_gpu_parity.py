@@ -188,6 +188,46 @@ def test_chunk_fwd_is_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+@pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32", "segment_scan", "unbounded",
+                                  "decode", "decode_unbounded"])
+def test_absent_A_log_is_zero(path):
+    """A_log = NULL means A_h = 0 for every head: the same results, bit for bit,
+    as an all-zero A_log, on the prefill paths and the decode step."""
+    import linear_attention_fwd_amd as kda
+    import torch
+    from kda_testlib import gpu_inputs
+    print(f"[case] A_log absent, path {path}", flush=True)
+    if path.startswith("decode"):
+        inp = kda_gen.make_decode(58, N=7, H=3, W=4, dtype="bf16", accepted=[0, 4, 2, 1, 3, 4, 0])
+        unb = path == "decode_unbounded"
+        outs = []
+        for A in (torch.zeros(inp.H, dtype=torch.float32, device="cuda"), None):
+            t = decode_gpu_inputs(inp)
+            o = kda.kda_decode_step(t["state"], t["cq"], t["ck"], t["cv"], t["cz"], t["cbeta"],
+                                    t["accepted"], t["nq"], t["nk"], t["nv"], t["nz"],
+                                    t["nbeta"], A, inp.g_min, unbounded_gate=unb)
+            torch.cuda.synchronize()
+            outs.append((kda_gen.from_torch(o), kda_gen.from_torch(t["state"])))
+    else:
+        inp = kda_gen.make_prefill(38, 600, 3, "bf16", lengths=[300, 0, 299, 1], s0_std=0.02,
+                                   s0_docs="all")
+        t = gpu_inputs(inp)
+        args = (t["q"], t["k"], t["v"], t["z"], t["beta"])
+        compute = 1 if path == "fp32" else 0
+        outs = []
+        for A in (torch.zeros(inp.H, dtype=torch.float32, device="cuda"), None):
+            if path == "segment_scan":
+                o, S = kda.kda_segment_scan(*args, A, inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                            n_segments=4)
+            else:
+                o, S = kda.kda_chunk_fwd(*args, A, inp.g_min, t["S0"], t["cu"], t["cu_host"],
+                                         compute=compute, unbounded_gate=path == "unbounded",
+                                         workspace=False if path == "fused" else None)
+            torch.cuda.synchronize()
+            outs.append((kda_gen.from_torch(o), kda_gen.from_torch(S)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
 @pytest.mark.parametrize("path", ["two_kernel", "fused", "fp32", "checkpoints", "noalloc",
                                   "segment_scan", "segment_scan_fp32"])
 def test_prefill_without_final_state(path):
