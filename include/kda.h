@@ -138,7 +138,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_log
                   float *final_state, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kda_chunk_fwd's two-kernel path needs for N documents of T
- * tokens in total and H heads: one 62 KiB image per head and chunk slot,
+ * tokens in total and H heads: one 61 KiB image per head and chunk slot,
  * (floor(T / 64) + N) slots per head, then 4 bytes per document (rounded up to
  * 256) for the order in which the recurrence takes the documents (longest
  * first; the order does not change any result).  0 for invalid sizes. */
@@ -178,7 +178,7 @@ int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const voi
  * kda_chunk_prep: token-parallel chunk prep over every (head, chunk) -- gate and
  * in-chunk cumulative decay, decay factors, intra-chunk products and the UT
  * transform ("序列维度（下）", sections "UT 变换" and "数值问题"; SemiAnalysis page,
- * "FlashKDA 算法") -- written as one 62 KiB chunk image per (head, chunk slot)
+ * "FlashKDA 算法") -- written as one 61 KiB chunk image per (head, chunk slot)
  * into workspace (kda_chunk_fwd_workspace_size bytes, 256-byte aligned).
  *
  * kda_chunk_recurrence: the serial chunk recurrence of every (document, head)

@@ -87,7 +87,7 @@ struct SplitParams {
 };
 // Bytes of one chunk image (the recurrence operands of one (head, chunk);
 // the layout is ChunkImage in kda_split.hip, which checks this size).
-constexpr int64_t CHUNK_IMAGE_BYTES = 63488;
+constexpr int64_t CHUNK_IMAGE_BYTES = 62464;
 // chunk images [H, n_slots, image], then the document order (4 N bytes,
 // rounded up to 256)
 inline size_t split_order_offset(int64_t T, int N, int H) {

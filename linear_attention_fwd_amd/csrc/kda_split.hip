@@ -44,7 +44,7 @@ struct __align__(16) ChunkImage {
   bf16_t Mqk[PackedLower::ELEMS];    // M_qk
   bf16_t INVb[PackedLower::ELEMS];   // INV Diag(beta)
   float gamC[D];                     // gamma^C
-  float pad[384];                    // the image is a whole number of 1 KB copy blocks
+  float pad[128];                    // the image is a whole number of 1 KB copy blocks
 };
 constexpr int IMG_BYTES = (int)sizeof(ChunkImage);
 constexpr int IMG_BLOCKS = IMG_BYTES / 1024;

@@ -109,7 +109,7 @@ def test_segment_scan_workspace_checks(lib):
     slots = 128 // 64 + 1                                    # 3 chunk slots -> 3 segments
     # images + segment pairs, and pairs + entry states of the 2 groups of 2 segments
     # the pairs are scanned in
-    need_bf16 = slots * 4 * 63488 + 256 + 3 * 4 * 128 * 256 * 4 + 2 * 4 * 128 * 384 * 4
+    need_bf16 = slots * 4 * 62464 + 256 + 3 * 4 * 128 * 256 * 4 + 2 * 4 * 128 * 384 * 4
     need_f32 = 4 * 4 * 128 * 384 * 4                         # 4 token segments
     assert need == max(need_bf16, need_f32)
     assert lib.kda_segment_scan_workspace_size(0, 128, 4, 4, 128, 128) == 0
@@ -126,14 +126,14 @@ def test_segment_scan_workspace_checks(lib):
 
 
 def test_chunk_fwd_workspace_checks(lib):
-    # one 62 KiB chunk image per head and slot, floor(T / 64) + N slots per head,
+    # one 61 KiB chunk image per head and slot, floor(T / 64) + N slots per head,
     # then the document order (4 bytes per document, rounded up to 256)
     need = lib.kda_chunk_fwd_workspace_size(1, 128, 4, 128, 128)
-    assert need == (128 // 64 + 1) * 4 * 63488 + 256
+    assert need == (128 // 64 + 1) * 4 * 62464 + 256
     assert lib.kda_chunk_fwd_workspace_size(3, 1000, 2, 128, 128) == \
-        (1000 // 64 + 3) * 2 * 63488 + 256
+        (1000 // 64 + 3) * 2 * 62464 + 256
     assert lib.kda_chunk_fwd_workspace_size(65, 1000, 2, 128, 128) == \
-        (1000 // 64 + 65) * 2 * 63488 + 512
+        (1000 // 64 + 65) * 2 * 62464 + 512
     assert lib.kda_chunk_fwd_workspace_size(0, 128, 4, 128, 128) == 0
     assert lib.kda_chunk_fwd_workspace_size(1, 128, 4, 64, 128) == 0
     # the two-kernel path (bf16, compute AUTO) refuses a short or misaligned workspace
@@ -424,9 +424,9 @@ def test_checkpoint_indices_are_unique_and_in_range(lib, lengths, interval):
 @settings(max_examples=60, deadline=None)
 @given(N=st.integers(1, 5000), T=st.integers(0, 1 << 24), H=st.integers(1, 128))
 def test_workspace_size_formula(lib, N, T, H):
-    """One 62 KiB image per head and chunk slot (floor(T / 64) + N slots), then
+    """One 61 KiB image per head and chunk slot (floor(T / 64) + N slots), then
     4 bytes per document rounded up to 256; no 32-bit overflow."""
-    want = (T // 64 + N) * H * 63488 + (4 * N + 255) // 256 * 256
+    want = (T // 64 + N) * H * 62464 + (4 * N + 255) // 256 * 256
     assert lib.kda_chunk_fwd_workspace_size(N, T, H, 128, 128) == want
 
 

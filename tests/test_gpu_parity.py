@@ -140,7 +140,7 @@ def test_document_order(case):
     kda.kda_chunk_prep(t["q"], t["k"], t["z"], t["beta"], ws, t["A_log"], inp.g_min, t["cu"],
                        t["cu_host"])
     torch.cuda.synchronize()
-    off = (inp.T // 64 + inp.N) * inp.H * 63488
+    off = (inp.T // 64 + inp.N) * inp.H * 62464
     assert nbytes == off + (4 * inp.N + 255) // 256 * 256
     order = ws[off:off + 4 * inp.N].cpu().numpy().view(np.int32)
     if case == "sorted":
