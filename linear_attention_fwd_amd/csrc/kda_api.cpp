@@ -555,9 +555,16 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     p.gate = gate;
     hipError_t e = kda::launch_chunk_prep(p, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan prep");
-    p.rmode = 2;  // A: segment pairs; resets at document starts are folded into them
-    e = kda::launch_chunk_recurrence(p, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
+    // Only the entry states of groups 1 .. n_groups - 1 come from pairs, so the
+    // segments of the last group need none: pairs and their composition cover
+    // the first n_groups - 1 groups.
+    const int64_t paired = (n_groups - 1) * glen;  // < sp.n_seg
+    if (paired > 0) {
+      p.rmode = 2;  // A: segment pairs; resets at document starts are folded into them
+      p.n_seg = (int)paired;
+      e = kda::launch_chunk_recurrence(p, st);
+      if (e != hipSuccess) return hip_fail(e, "kda_segment_scan pairs");
+    }
     // B: entry states E_0 = 0, E_{j+1} = M_j E_j + S~_j (the first chunk is a
     // document start, so E_0 never matters), for the first segment of each
     // group of glen segments: the pairs of a group are composed into one, and
@@ -565,22 +572,25 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     const int n_cu = kda_default_segments();  // compute units, or an error status
     if (n_cu < 0) return n_cu;
     kda::ScanChains sc{};
-    sc.pairs = pairs;
     sc.H = H;
-    sc.n_pairs = (int)sp.n_seg;
-    sc.chain_len = (int)glen;
-    sc.n_chains = (int)n_groups;
-    sc.ncols = 2 * kD;
-    sc.mode = 1;  // B1: compose each group of pairs
-    sc.composed = gpairs;
-    e = kda::launch_scan_chains(sc, n_cu, st);
-    if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group pairs");
-    sc.pairs = gpairs;  // B2: entry state of each group
-    sc.n_pairs = (int)n_groups;
+    if (paired > 0) {
+      sc.pairs = pairs;
+      sc.n_pairs = (int)paired;
+      sc.chain_len = (int)glen;
+      sc.n_chains = (int)(n_groups - 1);
+      sc.ncols = 2 * kD;
+      sc.mode = 1;  // B1: compose each group of pairs
+      sc.composed = gpairs;
+      e = kda::launch_scan_chains(sc, n_cu, st);
+      if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group pairs");
+    }
+    sc.pairs = gpairs;  // B2: entry state of each group (the last one after the last pair)
+    sc.n_pairs = (int)(n_groups - 1);
     sc.chain_len = (int)n_groups;
     sc.n_chains = 1;
     sc.ncols = kD;
     sc.mode = 0;
+    sc.write_final = 1;
     sc.states = gentry;
     e = kda::launch_scan_chains(sc, n_cu, st);
     if (e != hipSuccess) return hip_fail(e, "kda_segment_scan scan");

@@ -121,6 +121,7 @@ struct ScanChains {
   int n_chains;
   int ncols;          // 128 (states) or 256 (compose)
   int mode;           // 0: write the state before each pair to states[i]; 1: compose
+  int write_final;    // mode 0: also write the state after a chain's last pair to states[last]
   const float *init;  // mode 0: [n_chains, H, D, D] chain start states, or nullptr (0)
   float *states;      // mode 0: [n_pairs, H, D, D]
   float *composed;    // mode 1: [n_chains, H, D, 2D]

@@ -171,7 +171,9 @@ kda_pair_scan_kernel(const float *__restrict__ pairs, const float *__restrict__ 
 // walks pairs first..last (last exclusive) of the pair array and keeps a state
 // X with ncols columns:
 //   mode 0 (states): X starts from init[chain] (or 0) and the state before each
-//     pair, X_i, is written to states[i]; X <- M_i X + S~_i;
+//     pair, X_i, is written to states[i]; X <- M_i X + S~_i; with write_final
+//     the state after the chain's last pair is written too, to states[last]
+//     (a chain of no pairs then writes its start state);
 //   mode 1 (compose): X = [S~ | M] of the first pair, then X <- M_i X + [S~_i | 0]
 //     for the others, i.e. the pairs composed into one; written to composed[chain].
 // One workgroup per (chain, head, slice of 16 CT columns of X) with 8 / RT
@@ -205,7 +207,8 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
   const int c0 = COLS * sb.slice;  // first column of the slice (S~ part below D, M part from D on)
   const int first = chain * sc.chain_len;
   const int last = min(first + sc.chain_len, sc.n_pairs);
-  if (first >= last) return;
+  const bool final_write = sc.mode == 0 && sc.write_final;
+  if (first >= last && !final_write) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -356,6 +359,7 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
   }
   if (n < nsteps) body(n, ops[0], ops[1]);
   if (sc.mode == 1) write_state(sc.composed + ((int64_t)chain * sc.H + h) * (D * 2 * D), 2 * D, X);
+  if (final_write) write_state(sc.states + ((int64_t)max(first, last) * sc.H + h) * (D * D), D, X);
 }
 
 // A step is bound by the latency of its dependent loads and products, which
