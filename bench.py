@@ -245,16 +245,22 @@ def context_line(which, inp, np, torch, kda_gen, kda, dev, timer, args):
     o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
     if which == "long":
-        n_seg = kda.kda_default_segments()
-        ws = torch.empty(kda.kda_segment_scan_workspace_size(N, T, H, n_seg), dtype=torch.uint8,
+        n_cu = kda.kda_default_segments()
+        n_seg = -(-n_cu // H)  # the library's default plan: one (segment, head) per compute unit
+        plan = (f"{n_seg} segments (one per compute unit for each of the {H} heads) scanned in "
+                f"one level" if n_seg <= 32 else f"{n_cu} segments in groups")
+        ws = torch.empty(kda.kda_segment_scan_workspace_size(N, T, H, 0), dtype=torch.uint8,
                          device=dev)
+        ws_cu = torch.empty(kda.kda_segment_scan_workspace_size(N, T, H, n_cu),
+                            dtype=torch.uint8, device=dev)
 
-        def step():
+        def step(n_segments=0, w=ws):
             kda.kda_segment_scan(t["q"], t["k"], t["v"], t["z"], t["beta"], A_log, inp.g_min, S0,
-                                 cu, cu_host, n_segments=n_seg, o=o, final_state=fin, workspace=ws)
+                                 cu, cu_host, n_segments=n_segments, o=o, final_state=fin,
+                                 workspace=w)
         config = {"workload": f"long prefill, one sequence B=1 H={H} T={T} d_k=d_v=128 C=64, bf16 "
-                              f"inputs, fp32 state; segment scan with {n_seg} segments (one per "
-                              f"compute unit): segment pairs, pair scan, re-run",
+                              f"inputs, fp32 state; segment scan, default plan: {plan}: segment "
+                              f"pairs, pair scan, re-run",
                   "global_batch": 1, "seq_len": T, "heads": H, "parallelism": "single GPU"}
     else:
         ws = torch.empty(kda.kda_chunk_fwd_workspace_size(N, T, H), dtype=torch.uint8, device=dev)
@@ -268,12 +274,19 @@ def context_line(which, inp, np, torch, kda_gen, kda, dev, timer, args):
                   "global_batch": N, "seq_len": T, "heads": H, "parallelism": "single GPU"}
     steps = max(20, args.steps // 2)
     med, mean, wall = timer.run(step, steps, max(3, args.warmup // 4))
+    extra = {}
+    if which == "long":
+        # the pages' literal split, one segment per compute unit (two-level scan)
+        cu_med, _, _ = timer.run(lambda: step(n_cu, ws_cu), steps, max(3, args.warmup // 4))
+        extra["one_segment_per_compute_unit"] = {"segments": n_cu, "ms": cu_med,
+                                                 "tokens_per_s": T / (cu_med * 1e-3)}
+        del ws_cu
     chunk_heads = chunk_heads_of(np, inp.cu_seqlens if N > 1 else None, T, H)
     by, fl, t_model = model_bound(chunk_heads, N * H)
     alg = prefill_algorithmic_bytes(T, H, N, has_s0=inp.S0 is not None)
     del t, o, fin, ws
     torch.cuda.empty_cache()
-    return {
+    res = {
         "metric": f"KDA {which} prefill tokens/s", "value": T / (med * 1e-3), "unit": "tokens/s",
         "steps": steps, "ms_per_step": med, "ms_mean": mean, "ms_wall": wall,
         "dtype": "bf16", "data": "synthetic", "config": config,
@@ -286,6 +299,8 @@ def context_line(which, inp, np, torch, kda_gen, kda, dev, timer, args):
                            "achieved_TFLOPs": fl / (med * 1e-3) / 1e12,
                            "t_bound_ms": t_model * 1e3, "frac": t_model / (med * 1e-3)},
     }
+    res.update(extra)
+    return res
 
 
 def main():

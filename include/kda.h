@@ -269,18 +269,23 @@ int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const v
  *   B. per head, entry states are scanned: E_{j+1} = M_j E_j + S~_j;
  *   C. every segment is re-run from its exact entry state, producing O and the
  *      final state of every document.
- * On the bf16 path, B and C work on groups of about sqrt(n_segments)
- * consecutive segments: the pairs of a group are composed into one pair, the
- * group pairs are scanned into the entry state of each group, and the segments
- * of a group are re-run back to back from it (each then starts from the state
- * the previous one ends with, its exact entry state).
+ * On the bf16 path with a given n_segments, B and C work on groups of about
+ * sqrt(n_segments) consecutive segments: the pairs of a group are composed into
+ * one pair, the group pairs are scanned into the entry state of each group, and
+ * the segments of a group are re-run back to back from it (each then starts
+ * from the state the previous one ends with, its exact entry state); the last
+ * group's segments need no pair.
  * With bf16 arithmetic (dtype KDA_BF16, compute AUTO) the segments are equal
  * ranges of 64-token chunk slots (see kda_chunk_fwd_workspace_size) and all
  * three phases run on the two kernels of kda_chunk_fwd over one chunk prep;
  * with fp32 arithmetic they are equal token ranges (the last one ragged) run by
  * the fused kernel, and a document starting exactly on a segment boundary
  * resets the scan to its initial state.
- * n_segments <= 0 means one segment per compute unit of the current device.
+ * n_segments <= 0 chooses the count: on the bf16 path, one (segment, head) per
+ * compute unit, ceil(CUs / H) segments, each its own group (no composition),
+ * while that is at most 32, else one segment per compute unit in groups as
+ * above; on the fp32 path one segment per compute unit.  Every choice gives
+ * the same operator (results differ by rounding only).
  * workspace: device memory of at least kda_segment_scan_workspace_size() bytes,
  * 256-byte aligned; its contents on entry are ignored. */
 size_t kda_segment_scan_workspace_size(int32_t N, int64_t T, int32_t H, int32_t n_segments,
@@ -294,8 +299,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
                      int32_t n_segments, void *o, float *final_state, void *workspace,
                      size_t workspace_bytes, void *stream);
 
-/* Number of segments kda_segment_scan uses for n_segments <= 0 (the compute-unit
- * count of the current device), or a negative kda_status. */
+/* The compute-unit count of the current device (the segment count
+ * kda_segment_scan's fp32 path uses for n_segments <= 0, and the bf16 path's
+ * for H < CUs / 32), or a negative kda_status. */
 int kda_default_segments(void);
 
 /* ------------------------------------------------------------------------- */

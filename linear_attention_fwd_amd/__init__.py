@@ -433,12 +433,14 @@ def kda_segment_scan(q, k, v, g_logits, beta, A_log=None, g_min: float = -5.0,
                      final_state=None, raw_inputs: bool = False, unbounded_gate: bool = False):
     """Prefill via per-segment affine pairs, an on-device pair scan and a re-run
     from exact entry states.  Same tensors as ``kda_chunk_fwd``; n_segments <= 0
-    uses one segment per compute unit.  Returns (o, final_state)."""
+    lets the library choose the count (bf16: one (segment, head) per compute unit
+    while that is at most 32 segments; fp32: one segment per compute unit).
+    Returns (o, final_state)."""
     torch = _torch()
     lib = load_library()
     T, H, dk, dv, N, cu_dev, cu_host = _prefill_common(q, k, v, g_logits, beta, A_log,
                                                        initial_state, cu_seqlens, cu_seqlens_host)
-    n_seg = n_segments if n_segments > 0 else kda_default_segments()
+    n_seg = max(int(n_segments), 0)  # 0: the library's plan (see include/kda.h)
     need = kda_segment_scan_workspace_size(N, T, H, n_seg, dk, dv)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -225,11 +225,32 @@ int64_t max_scan_groups(int64_t n_max) {
     if (scan_groups(n) > m) m = scan_groups(n);
   return m;
 }
-size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, int64_t requested) {
-  const int64_t n_max = max_split_segments(T, N, requested);
+// The two-kernel path's segment count for a request (n_segments <= 0: the
+// default) and whether its pairs are scanned in one level.  By default each
+// (segment, head) unit gets a compute unit: n = ceil(CUs / H) segments, one
+// level (every segment its own group), while that keeps the scan's chain at
+// 32 pairs or fewer; the group pairs are then the segment pairs, no pairs are
+// composed, and the re-run's units fill the device.  (On the long prefill,
+// T = 262144 with H = 8: 32 segments in one level, 2.02 ms, against 256 in two
+// levels, 2.14 ms: the composition of 240 pairs costs more than a longer scan
+// saves.)  Beyond 32, and for any count the caller gives, one segment per
+// requested unit and two levels.
+struct SplitRequest {
+  int64_t n;
+  bool one_level;
+};
+SplitRequest split_request(int32_t n_segments, int32_t H, int cus) {
+  if (n_segments > 0) return SplitRequest{n_segments, false};
+  const int64_t per_head = ((int64_t)cus + H - 1) / H;
+  if (per_head <= 32) return SplitRequest{per_head, true};
+  return SplitRequest{cus, false};
+}
+size_t split_scan_workspace(int64_t T, int32_t N, int32_t H, const SplitRequest &r) {
+  const int64_t n_max = max_split_segments(T, N, r.n);
+  const int64_t g_max = r.one_level ? n_max : max_scan_groups(n_max);
   // chunk images, segment pairs [., D, 2D], group pairs and group entry states
   return kda::split_workspace_bytes(T, N, H) + (size_t)n_max * H * kD * 2 * kD * sizeof(float) +
-         scan_workspace(max_scan_groups(n_max), H);
+         scan_workspace(g_max, H);
 }
 
 }  // namespace
@@ -480,15 +501,15 @@ int kda_default_segments(void) {
 size_t kda_segment_scan_workspace_size(int32_t N, int64_t T, int32_t H, int32_t n_segments,
                                        int32_t dk, int32_t dv) {
   if (N <= 0 || T < 0 || H <= 0 || dk != kD || dv != kD) return 0;
-  int64_t req = n_segments;
-  if (req <= 0) {
-    const int cus = kda_default_segments();
+  int cus = 0;
+  if (n_segments <= 0) {
+    cus = kda_default_segments();
     if (cus < 0) return 0;
-    req = cus;
   }
   // enough for either arithmetic path
+  const int64_t req = n_segments > 0 ? n_segments : cus;
   const size_t fused = scan_workspace(plan_segments(T > 0 ? T : 1, req).n_seg, H);
-  const size_t split = split_scan_workspace(T, N, H, req);
+  const size_t split = split_scan_workspace(T, N, H, split_request(n_segments, H, cus));
   return fused > split ? fused : split;
 }
 
@@ -513,27 +534,30 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
   }
   const bool f32c = compute == KDA_COMPUTE_F32 || dtype == KDA_F32;
   if (raw && f32c && dtype == KDA_BF16) return raw_unsupported("kda_segment_scan");
-  int64_t req = n_segments;
-  if (req <= 0) {
-    const int cus = kda_default_segments();
+  int cus = 0;
+  if (n_segments <= 0) {
+    cus = kda_default_segments();
     if (cus < 0) return cus;
-    req = cus;
   }
+  const int64_t req = n_segments > 0 ? n_segments : cus;  // the fused path's count
   hipStream_t st = (hipStream_t)stream;
   if (T > 0 && !f32c) {
     // two-kernel path: chunk prep over all chunks, segment pairs and the re-run
     // on the recurrence kernel; segments are ranges of chunk slots
-    const SegPlan sp = plan_segments(used_chunk_slots(T, N, cu_seqlens_host), req);
+    const SplitRequest sr = split_request(n_segments, H, cus);
+    const SegPlan sp = plan_segments(used_chunk_slots(T, N, cu_seqlens_host), sr.n);
     if (sp.n_seg * H > kMaxSegHeads)
       return fail(KDA_ERR_SHAPE, "segments * H = %lld exceeds %lld (one launch)",
                   (long long)(sp.n_seg * H), (long long)kMaxSegHeads);
-    const size_t need = split_scan_workspace(T, N, H, req);
+    const size_t need = split_scan_workspace(T, N, H, sr);
     if (!workspace || workspace_bytes < need)
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     // the buffers are laid out for the largest plan the workspace size allows for
-    const int64_t n_max = max_split_segments(T, N, req), g_max = max_scan_groups(n_max);
-    const int64_t glen = scan_group_len(sp.n_seg), n_groups = scan_groups(sp.n_seg);
+    const int64_t n_max = max_split_segments(T, N, sr.n);
+    const int64_t g_max = sr.one_level ? n_max : max_scan_groups(n_max);
+    const int64_t glen = sr.one_level ? 1 : scan_group_len(sp.n_seg);
+    const int64_t n_groups = (sp.n_seg + glen - 1) / glen;
     if (n_groups * H > kMaxGroupHeads)
       return fail(KDA_ERR_SHAPE, "segment groups * H = %lld exceeds %lld (one launch)",
                   (long long)(n_groups * H), (long long)kMaxGroupHeads);
@@ -573,7 +597,7 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
     if (n_cu < 0) return n_cu;
     kda::ScanChains sc{};
     sc.H = H;
-    if (paired > 0) {
+    if (paired > 0 && glen > 1) {
       sc.pairs = pairs;
       sc.n_pairs = (int)paired;
       sc.chain_len = (int)glen;
@@ -584,7 +608,9 @@ int kda_segment_scan(const void *q, const void *k, const void *v, const void *g_
       e = kda::launch_scan_chains(sc, n_cu, st);
       if (e != hipSuccess) return hip_fail(e, "kda_segment_scan group pairs");
     }
-    sc.pairs = gpairs;  // B2: entry state of each group (the last one after the last pair)
+    // B2: entry state of each group (the last one after the last pair); groups
+    // of one segment scan the segment pairs themselves
+    sc.pairs = glen > 1 ? gpairs : pairs;
     sc.n_pairs = (int)(n_groups - 1);
     sc.chain_len = (int)n_groups;
     sc.n_chains = 1;

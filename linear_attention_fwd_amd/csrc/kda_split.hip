@@ -251,10 +251,11 @@ __global__ void __launch_bounds__(FWD_THREADS, 3) kda_chunk_prep_kernel(SplitPar
 //
 // A compute wave owns NT tiles of 16 state columns, so a workgroup owns 64 NT
 // columns.  Every workgroup copies the whole image of each chunk, whatever its
-// column count, and that copy bounds the time per chunk; so where there are
-// fewer (item, head) units than compute units, NT = 1 spreads each unit over
-// two workgroups (four for segment pairs, whose state is 256 columns wide),
-// and where there are more, NT = 2 halves the number of chunk steps.  The
+// column count, and that copy bounds the time per chunk; so where NT = 2
+// workgroups (one per (item, head) unit, two for a segment pair's 256 columns)
+// would leave compute units idle, NT = 1 spreads each unit over two
+// workgroups (four for pairs), and where they fill the device, NT = 2 halves
+// the number of chunk steps.  The
 // workgroups of one unit share an XCD (blockIdx % 8), so the image reaches
 // them from one L2.
 // ---------------------------------------------------------------------------
@@ -821,11 +822,12 @@ static int device_cus() {
 }
 
 hipError_t launch_chunk_recurrence(const SplitParams &p, hipStream_t stream) {
-  // Two column tiles per compute wave once the (item, head) units alone fill
-  // the device; the workgroups of one unit share an XCD
+  // Two column tiles per compute wave once the workgroups that gives (one per
+  // unit, two for a pair's 256 columns) fill the device; the workgroups of one
+  // unit share an XCD
   const int units = (p.rmode == 0 ? p.N : p.n_seg) * p.H;
   const int cus = device_cus();
-  const bool wide = units >= (cus > 0 ? cus : 256);  // the units fill the device
+  const bool wide = units * (p.rmode == 2 ? 2 : 1) >= (cus > 0 ? cus : 256);
   const int groups = (units + 7) / 8;
   const int nsplit = (p.rmode == 2 ? 4 : 2) / (wide ? 2 : 1);
   const dim3 grid((unsigned)(groups * 8 * nsplit));

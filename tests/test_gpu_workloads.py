@@ -56,27 +56,30 @@ def test_single_sequence_workload():
 
 
 def test_long_prefill_segment_scan_workload():
-    """One TP rank's 8 heads over 262144 tokens, one segment per compute unit; the
-    result must match a single serial pass (the oracle, and the chunk kernel)."""
+    """One TP rank's 8 heads over 262144 tokens: the default plan (one (segment,
+    head) per compute unit, one-level scan) and one segment per compute unit
+    (256, two-level scan); the result must match a single serial pass (the
+    oracle, and the chunk kernel)."""
     import linear_attention_fwd_amd as kda
     inp = kda_gen.workload(2)
-    n_seg = kda.kda_default_segments()
-    print(f"[case] long prefill T=262144 H=8, {n_seg} segments", flush=True)
+    n_cu = kda.kda_default_segments()
     t = gpu_inputs(inp)
-    o, S = gpu_segment_scan(inp, n_segments=0, t=t)
     o_ref, S_ref = oracle_forward(inp, group=8)
-    eo, es = _report("segment scan vs oracle", o, o_ref, S, S_ref, inp.cu_seqlens)
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for n_seg in (0, n_cu):
+        print(f"[case] long prefill T=262144 H=8, n_segments={n_seg}", flush=True)
+        o, S = gpu_segment_scan(inp, n_segments=n_seg, t=t)
+        eo, es = _report("segment scan vs oracle", o, o_ref, S, S_ref, inp.cu_seqlens)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
     o1, S1 = gpu_chunk_fwd(inp, t=t)
     eo1, es1 = _report("serial chunk kernel vs oracle", o1, o_ref, S1, S_ref, inp.cu_seqlens)
     assert eo1 <= TOL_BF16 and es1 <= TOL_BF16
 
 
 def test_long_prefill_long_memory_segment_scan():
-    """The long-prefill shape (T=262144, H=8, one segment per compute unit) with
-    decays of about 1e-4 to 5e-3 per token (z ~ N(-9, 1), A = 0): states
-    remember across the 1024-token segments and the groups of 16 segments, so
-    the composed pairs and the group scan decide the outputs, unlike under
+    """The long-prefill shape (T=262144, H=8; the default plan of 32 segments
+    and one segment per compute unit) with decays of about 1e-4 to 5e-3 per
+    token (z ~ N(-9, 1), A = 0): states remember across segments and groups, so
+    the pairs and the scans decide the outputs (both plans), unlike under
     the workload's own decays (about -2.5 per token), which forget an entry
     state within a few tokens."""
     inp = kda_gen.make_prefill(52, 262144, 8, "bf16", A_std=0.0, z_mean=-9.0, z_std=1.0,
@@ -84,11 +87,14 @@ def test_long_prefill_long_memory_segment_scan():
     g = oracle.gate(inp.z.f64()[:4096:64], inp.A_log, inp.g_min)
     print(f"[case] long prefill, long memory: per-token decay median {np.median(-g):.1e}, "
           f"90% in [{np.quantile(-g, 0.05):.1e}, {np.quantile(-g, 0.95):.1e}]", flush=True)
+    import linear_attention_fwd_amd as kda
     t = gpu_inputs(inp)
-    o, S = gpu_segment_scan(inp, n_segments=0, t=t)
     o_ref, S_ref = oracle_forward(inp, group=8)
-    eo, es = _report("segment scan vs oracle", o, o_ref, S, S_ref, inp.cu_seqlens)
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for n_seg in (0, kda.kda_default_segments()):
+        print(f"    n_segments={n_seg}", flush=True)
+        o, S = gpu_segment_scan(inp, n_segments=n_seg, t=t)
+        eo, es = _report("segment scan vs oracle", o, o_ref, S, S_ref, inp.cu_seqlens)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
     o1, S1 = gpu_chunk_fwd(inp, t=t)
     eo1, es1 = _report("serial chunk kernel vs oracle", o1, o_ref, S1, S_ref, inp.cu_seqlens)
     assert eo1 <= TOL_BF16 and es1 <= TOL_BF16
