@@ -368,8 +368,13 @@ __global__ void __launch_bounds__(512 / RT) kda_scan_chains_kernel(ScanChains sc
 // whole long-prefill step; 32-column slices, four per CU, 2.17 ms; 16-column
 // slices, eight per CU, 2.26 ms).  So 64-column slices are taken only where
 // they already give four per CU, 32-column slices where they give two, and
-// chains too few for that (the scan of the group pairs) take 16 columns per
-// workgroup.  (128-column slices of 8 waves timed no faster.)
+// chains too few for that (the scan of the segment or group pairs) take 16
+// columns per workgroup in 8 waves of one row tile each: with one workgroup
+// per compute unit, more waves with shorter MFMA chains and fewer loads each
+// step faster (31 steps of the long prefill's pair scan: 74.6 us against
+// 90.9 for 4 waves of two row tiles, identical results; loading the operands
+// two steps ahead instead of one gained nothing).  (128-column slices of 8
+// waves timed no faster.)
 hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream) {
   const int64_t units = (int64_t)sc.n_chains * sc.H;
   if (units * (sc.ncols / 64) >= 4 * (int64_t)n_cu) {
@@ -379,7 +384,7 @@ hipError_t launch_scan_chains(const ScanChains &sc, int n_cu, hipStream_t stream
     hipLaunchKernelGGL((kda_scan_chains_kernel<2, 2>), dim3(scan_grid(units, sc.ncols / 32)), dim3(256),
                        0, stream, sc);
   } else {
-    hipLaunchKernelGGL((kda_scan_chains_kernel<1, 2>), dim3(scan_grid(units, sc.ncols / 16)), dim3(256),
+    hipLaunchKernelGGL((kda_scan_chains_kernel<1, 1>), dim3(scan_grid(units, sc.ncols / 16)), dim3(512),
                        0, stream, sc);
   }
   return hipGetLastError();
