@@ -463,7 +463,7 @@ SCAN_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(SCAN_CASES))
-@pytest.mark.parametrize("n_seg", [1, 7, 64])
+@pytest.mark.parametrize("n_seg", [0, 1, 7, 64])
 def test_segment_scan_matches_oracle(name, n_seg):
     kw = dict(SCAN_CASES[name])
     seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
@@ -473,6 +473,40 @@ def test_segment_scan_matches_oracle(name, n_seg):
         _case(inp, compute)
         print(f"    n_segments={n_seg}", flush=True)
         o, S = gpu_segment_scan(inp, n_segments=n_seg, compute=compute)
+        _check_prefill(inp, o, S, _tols(inp, compute), ref)
+
+
+DEFAULT_PLAN_CASES = {
+    # n_segments = 0 with H >= CUs / 32: ceil(CUs / H) segments per head, each its
+    # own group, scanned in one level.  Document d's first chunk slot is
+    # floor(cu[d] / 64) + d.  At 256 CUs: H=8 asks for 32 segments over 46 used
+    # slots -> 23 segments of 2 slots, documents starting on segment boundaries
+    # (slots 12, 32, 34) and inside one (slot 15), an empty document between;
+    # H=12 asks for 22 -> 16 segments of 3 slots (long memory); H=40 asks for 7
+    # -> 7 of 5 slots, a one-token document on a boundary (slot 15) and the next
+    # document inside a segment (slot 16); H=96 asks for 3 -> 3 of 4 slots.
+    "h8_varlen": dict(seed=71, T=2600, H=8, dtype="bf16", lengths=[704, 100, 0, 1000, 64, 732],
+                      s0_std=0.05, s0_docs="all"),
+    "h12_slow_decay": dict(seed=72, T=3000, H=12, dtype="bf16", z_mean=-6.0, s0_std=0.05,
+                           s0_docs="all"),
+    "h40_varlen": dict(seed=73, T=1800, H=40, dtype="bf16", lengths=[900, 1, 899],
+                       s0_std=0.05, s0_docs="all"),
+    "h96_single": dict(seed=74, T=700, H=96, dtype="bf16", s0_std=0.05, s0_docs="all"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEFAULT_PLAN_CASES))
+def test_segment_scan_default_plan(name):
+    """The default segment plan (one (segment, head) per compute unit, one level)
+    against the oracle, with bf16 and fp32 arithmetic."""
+    kw = dict(DEFAULT_PLAN_CASES[name])
+    seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
+    inp = kda_gen.make_prefill(seed, T, H, **kw)
+    ref = oracle_forward(inp)
+    for compute in (0, 1):
+        _case(inp, compute)
+        print("    n_segments=0", flush=True)
+        o, S = gpu_segment_scan(inp, n_segments=0, compute=compute)
         _check_prefill(inp, o, S, _tols(inp, compute), ref)
 
 
