@@ -247,7 +247,7 @@ def context_line(which, inp, np, torch, kda_gen, kda, dev, timer, args):
     if which == "long":
         n_cu = kda.kda_default_segments()
         n_seg = -(-n_cu // H)  # the library's default plan: one (segment, head) per compute unit
-        plan = (f"{n_seg} segments (one per compute unit for each of the {H} heads) scanned in "
+        plan = (f"{n_seg} segments per head, one (segment, head) per compute unit, scanned in "
                 f"one level" if n_seg <= 32 else f"{n_cu} segments in groups")
         ws = torch.empty(kda.kda_segment_scan_workspace_size(N, T, H, 0), dtype=torch.uint8,
                          device=dev)
@@ -276,7 +276,8 @@ def context_line(which, inp, np, torch, kda_gen, kda, dev, timer, args):
     med, mean, wall = timer.run(step, steps, max(3, args.warmup // 4))
     extra = {}
     if which == "long":
-        # the pages' literal split, one segment per compute unit (two-level scan)
+        # one segment per compute unit over all heads: as many segments per head as
+        # compute units (two-level scan)
         cu_med, _, _ = timer.run(lambda: step(n_cu, ws_cu), steps, max(3, args.warmup // 4))
         extra["one_segment_per_compute_unit"] = {"segments": n_cu, "ms": cu_med,
                                                  "tokens_per_s": T / (cu_med * 1e-3)}
