@@ -83,6 +83,55 @@ def test_prefill_graph_replays():
             assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
+def test_segment_scan_default_plan_graph_replays():
+    """kda_segment_scan with the default plan (n_segments = 0; at H = 8 one
+    (segment, head) per compute unit, scanned in one level), captured once: every
+    replay on new inputs equals the same eager call bit for bit."""
+    import torch
+    import linear_attention_fwd_amd as kda
+
+    def draw(seed):
+        return kda_gen.make_prefill(seed, 1500, 8, "bf16", lengths=[130, 0, 700, 1, 0, 669],
+                                    s0_std=0.02, s0_docs="all")
+
+    inp = draw(91)
+    print(f"[case] graph segment scan, default plan, T={inp.T} H={inp.H} N={inp.N}", flush=True)
+    t = gpu_inputs(inp)
+    args = lambda: (t["q"], t["k"], t["v"], t["z"], t["beta"], t["A_log"], inp.g_min, t["S0"],
+                    t["cu"], t["cu_host"])
+    ws = torch.empty(kda.kda_segment_scan_workspace_size(inp.N, inp.T, inp.H, 0),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((inp.T, inp.H, 128), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((inp.N, inp.H, 128, 128), dtype=torch.float32, device="cuda")
+    kda.kda_segment_scan(*args(), n_segments=0, o=o, final_state=S, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.kda_segment_scan(*args(), n_segments=0, o=o, final_state=S, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        new = draw(92 + r)
+        for name in ("q", "k", "v", "z", "beta"):
+            t[name].copy_(kda_gen.to_torch(getattr(new, name), "cuda"))
+        t["S0"].copy_(torch.from_numpy(new.S0).to("cuda"))
+        t["A_log"].copy_(torch.from_numpy(new.A_log).to("cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_S = kda_gen.from_torch(o), kda_gen.from_torch(S)
+        o_e, S_e = kda.kda_segment_scan(*args(), n_segments=0, workspace=ws)
+        torch.cuda.synchronize()
+        o_e, S_e = kda_gen.from_torch(o_e), kda_gen.from_torch(S_e)
+        print(f"    replay {r}", flush=True)
+        assert np.array_equal(got_o, o_e) and np.array_equal(got_S, S_e), r
+        if r == 0:
+            o_ref, S_ref = oracle_forward(new)
+            eo, _ = rel_l2_slices(o_e, o_ref, new.cu_seqlens)
+            es, _ = rel_l2_slices(S_e, S_ref, axis_tokens=False)
+            print(f"    O {eo:.3e}  S {es:.3e}", flush=True)
+            assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
 def test_decode_graph_replays():
     """The decode step with the next window, captured once: each replay advances
     the states in place exactly as the same eager call does on a copy of them."""
