@@ -492,6 +492,12 @@ DEFAULT_PLAN_CASES = {
     "h40_varlen": dict(seed=73, T=1800, H=40, dtype="bf16", lengths=[900, 1, 899],
                        s0_std=0.05, s0_docs="all"),
     "h96_single": dict(seed=74, T=700, H=96, dtype="bf16", s0_std=0.05, s0_docs="all"),
+    # the same plan with the unbounded gate (strong decays) and on raw inputs
+    "h8_unbounded": dict(seed=75, T=2000, H=8, dtype="bf16", lengths=[1100, 0, 900],
+                         gate="softplus", z_mean=2.0, z_std=3.0, A_std=1.0, s0_std=0.05,
+                         s0_docs="all"),
+    "h8_raw": dict(seed=76, T=2000, H=8, dtype="bf16", lengths=[640, 1360], raw=True,
+                   s0_std=0.05, s0_docs="all"),
 }
 
 
@@ -503,7 +509,8 @@ def test_segment_scan_default_plan(name):
     seed, T, H = kw.pop("seed"), kw.pop("T"), kw.pop("H")
     inp = kda_gen.make_prefill(seed, T, H, **kw)
     ref = oracle_forward(inp)
-    for compute in (0, 1):
+    # raw bf16 inputs take bf16 arithmetic only (fp32 arithmetic on them is refused)
+    for compute in ((0,) if inp.raw else (0, 1)):
         _case(inp, compute)
         print("    n_segments=0", flush=True)
         o, S = gpu_segment_scan(inp, n_segments=0, compute=compute)
